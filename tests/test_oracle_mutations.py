@@ -1,0 +1,58 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a copy of the oracle's C source (on the CPU,
+in a temporary directory), builds it, and runs the pin suite against that copy in
+a subprocess: the suite must fail.  The unmodified oracle passes the same suite
+(tests/test_oracle_pins.py).
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "rpkv_oracle.c")
+
+MUTATIONS = {
+    "mask_off_by_one": ("int64_t hi = a + 1 < pb->key_hi ? a + 1 : pb->key_hi;",
+                        "int64_t hi = a < pb->key_hi ? a : pb->key_hi;"),
+    "top_left_alignment": ("const int64_t a = L - n + r;", "const int64_t a = r;"),
+    "gqa_modulo_map": ("kvh = h / G;", "kvh = h % Hkv;"),
+    "slot_ignores_page_size": ("return page * page_size + pos % page_size;",
+                               "return page + pos % page_size;"),
+    "scale_dropped": ("x[j - lo] = pb->scale * dot;", "x[j - lo] = dot;"),
+    "max_not_subtracted": ("double w = exp(x[j - lo] - m);", "double w = exp(x[j - lo]);"),
+    "lse_sign": ("*lse = m + log(Z);", "*lse = m - log(Z);"),
+    "not_normalised": ("for (int32_t d = 0; d < D; ++d) out[d] /= Z;", ""),
+    "v_from_k_pool": ("out[d] += w * up(pb->vpool, vbase + d, pb->dtype);",
+                      "out[d] += w * up(pb->kpool, vbase + d, pb->dtype);"),
+    "query_row_uses_kv_head": ("const int64_t qbase = ((int64_t)t * Hq + h) * D;",
+                               "const int64_t qbase = ((int64_t)t * Hq + kvh) * D;"),
+    "merge_weight_sign": ("double w = exp(l - M);", "double w = exp(M - l);"),
+    "store_swaps_k_and_v": (
+        "memcpy((char *)kpool + s * row_bytes, (const char *)k + t * row_bytes, (size_t)row_bytes);",
+        "memcpy((char *)kpool + s * row_bytes, (const char *)v + t * row_bytes, (size_t)row_bytes);"),
+    "last_index_off_by_one": ("out[i] = (cu_q[i + 1] > cu_q[i]) ? cu_q[i + 1] - 1 : -1;",
+                              "out[i] = (cu_q[i + 1] > cu_q[i]) ? cu_q[i + 1] : -1;"),
+    "position_off_by_one": ("int32_t pos = num_computed[i] + r;",
+                            "int32_t pos = num_computed[i] + r + 1;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_fail_on_planted_mistake(name, tmp_path):
+    orig, repl = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(orig) == 1, f"mutation anchor not unique/present: {name}"
+    mutated = src.replace(orig, repl)
+    c = tmp_path / "mut.c"
+    so = tmp_path / "libmut.so"
+    c.write_text(mutated)
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-o", str(so), str(c),
+                           "-lm", "-lpthread"])
+    env = dict(os.environ, RPKV_ORACLE_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutation {name}:\n{r.stdout[-2000:]}"
