@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark: one batch step of ragged, paged, prefix-cached attention on one
+MI355X, through the library's C ABI.
+
+A step is the whole hot path for one batch of a 32-layer model: prepare_metadata
+once (host planning + one upload), then for each layer forward(q, k, v, layer) =
+store_kv of the step's K/V followed by attention (MFMA tiles, split-KV chunks,
+log-sum-exp merge).  Each layer has its own q/k/v/out and KV pools; pools are
+cycled so the working set between reuses exceeds the 256 MB Infinity Cache.
+Inputs are seeded synthetic tensors already resident in HBM.
+
+Default workload: the Llama-3-8B-shaped mixed layer (Hq=32, Hkv=8, D=128,
+page_size=16; query lens [2000, 512, 1 x 6]; decode histories uniform in
+[512, 4096]); value = algorithmic attention TFLOP/s (unmasked query-key pairs x
+4 x D x Hq) over the whole step.  --workload picks another of the five batches
+(the decode-heavy one reports KV-read GB/s).
+
+Prints ONE JSON line (rank 0) with the roofline of the dominant kernel, measured
+with HIP events on the launch stream in a second pass over the same steps, and
+the fp64 CPU oracle timed on the host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+LAYERS = 32
+
+WORKLOADS = {
+    "c1": (1, "c1_tiny_mixed_fp32: query lens [6,3,1], KV [6,7,9], Hq=4 Hkv=2 D=64 page_size=1, fp32"),
+    "c2": (2, "c2_llama3_8b_mixed: Hq=32 Hkv=8 D=128 page_size=16, query lens [2000,512,1x6], "
+              "prefills uncached, decode history U[512,4096], bf16"),
+    "c3": (3, "c3_decode_heavy: 256 decodes, KV U[1024,8192], Hq=32 Hkv=8 D=128 page_size=16, bf16"),
+    "c4": (4, "c4_chunked_prefill: 16 x (4096 cached + 512 new) + 32 decodes KV U[256,2048], "
+              "Hq=28 Hkv=4 D=128 page_size=16, bf16"),
+    "c5": (5, "c5_shared_prefix_cascade: 64 decodes sharing an 8192-token prefix, tails U[64,1024], "
+              "+ 2 x (28672 cached + 4096 new), Hq=64 Hkv=8 D=128 page_size=16, bf16"),
+}
+
+
+def algorithmic(spec, plan_info_members: int):
+    """Algorithmic work of one layer, split by kernel.
+
+    flops = 4*D*Hq*sum over requests of [n(L-n) + n(n+1)/2] (unmasked pairs).
+    KV bytes = 2*Hkv*D*b per unique slot read (a cascade's shared prefix once).
+    """
+    D, Hq, Hkv, b = spec.D, spec.Hq, spec.Hkv, spec.elem_bytes
+    n = spec.n.astype(np.int64)
+    L = spec.L.astype(np.int64)
+    pairs = n * (L - n) + n * (n + 1) // 2
+    G = spec.G
+    dec = (n > 0) & (n * G <= 16)
+    member = np.zeros(spec.bs, bool)
+    prefix = np.zeros(spec.bs, np.int64)
+    for (f, c, pl) in spec.groups:
+        for j in range(f, f + c):
+            if dec[j] and L[j] - n[j] >= pl:
+                member[j] = True
+                prefix[j] = pl
+    if plan_info_members == 0:
+        member[:] = False
+        prefix[:] = 0
+    row_kv = 2 * Hkv * D * b
+    flops_total = 4 * D * Hq * int(pairs.sum())
+    flops_prefill = 4 * D * Hq * int(pairs[~dec].sum() + (n * prefix)[member].sum())
+    dec_keys = int(np.where(member, L - prefix, L)[dec].sum())
+    kv_decode = row_kv * dec_keys
+    uniq = int(L.sum())
+    for (f, c, pl) in spec.groups:
+        uniq -= pl * (int(member[f:f + c].sum()) - 1) if member[f:f + c].sum() > 1 else 0
+    kv_total = row_kv * uniq
+    T = spec.T
+    io = T * spec.Hq * D * b * 2 + T * Hkv * D * b * 2 * 2   # q read, out write, k/v read + pool write
+    store_bytes = T * Hkv * D * b * 2 * 2
+    return dict(flops_total=flops_total, flops_prefill=flops_prefill, kv_decode=kv_decode,
+                kv_total=kv_total, bytes_total=kv_total + io, store_bytes=store_bytes)
+
+
+def cpu_baseline(spec, db, H):
+    """The fp64 oracle as it stands, on the host, over one layer of the batch
+    (every row for the small and mixed batches; a seeded row sample otherwise)."""
+    import oracle
+    from tests import gpu_harness as GH
+    rng = np.random.default_rng(0)
+    cores = min(16, os.cpu_count() or 1)
+    flops_of_row = None
+    if spec.T * spec.Hq * int(spec.L.max()) <= 3e9 / (4 * spec.D):  # whole layer <= ~3e9 pair-dims
+        reqs = list(range(spec.bs))
+        sub = GH.subproblem(spec, db, reqs)
+        rows = np.ones(sub.spec.T, bool)
+        sample = f"whole layer: all {spec.T} rows x {spec.Hq} heads"
+    else:
+        reqs = GH.pick_requests(spec, rng, max_reqs=16)
+        sub = GH.subproblem(spec, db, reqs)
+        rows = GH.pick_rows(spec, reqs, rng, per_req=4)[sub.token_map]
+        sample = (f"seeded sample: {int(rows.sum())} rows x {spec.Hq} heads of {len(reqs)} "
+                  f"requests")
+    s = sub.spec
+    t0 = time.perf_counter()
+    oracle.store_then_attend(s, sub.tensors, rows=rows, nthreads=cores)
+    dt = time.perf_counter() - t0
+    cu = s.cu_q
+    flops = 0
+    for i in range(s.bs):
+        for r in range(int(s.n[i])):
+            if rows[cu[i] + r]:
+                flops += 4 * s.D * s.Hq * (int(s.L[i]) - int(s.n[i]) + r + 1)
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=sample + f", fp64, {dt:.2f} s", seconds=dt)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+              "path shards by request or KV head with no exchange, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ragged_paged_kv_store_amd as rp
+    from tests import gpu_harness as H
+    from workloads import synth
+
+    torch.cuda.set_device(0)
+    cid, desc = WORKLOADS[args.workload]
+    spec = synth.full_config(cid)
+    stream = torch.cuda.current_stream()
+
+    # per-layer buffers: q/k/v/out per layer, pools cycled over npools sets
+    layer0 = H.device_contents(spec, seed=2024)
+    pool_bytes = 2 * layer0.kpool.numel() * layer0.kpool.element_size()
+    npools = int(min(LAYERS, max(2, math.ceil(2e9 / pool_bytes))))
+    pools = [(layer0.kpool, layer0.vpool)]
+    for j in range(1, npools):
+        d = H.device_contents(spec, seed=2024 + j)
+        pools.append((d.kpool, d.vpool))
+        del d
+    qkv = [(layer0.q, layer0.k, layer0.v)]
+    nq = min(LAYERS, 8)
+    for j in range(1, nq):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(77 + j)
+        dt = layer0.q.dtype
+        qkv.append(tuple(torch.randn(t.shape, generator=g, device="cuda").to(dt)
+                         for t in (layer0.q, layer0.k, layer0.v)))
+    outs = [torch.empty_like(layer0.q) for _ in range(nq)]
+    pt = layer0.page_table
+    sm = layer0.slot_mapping
+    plan = H.make_plan(spec)
+
+    def step():
+        plan.prepare(spec.cu_q, spec.L, pt, None, spec.groups, stream=stream)
+        for l in range(LAYERS):
+            kp, vp = pools[l % npools]
+            q, k, v = qkv[l % nq]
+            plan.forward(q, k, v, sm, kp, vp, outs[l % nq], spec.scale, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    info = plan.info()
+
+    # second pass over the same steps with HIP events around every launch
+    plan.timing_enable(True, max_launches=8 * LAYERS * args.steps + 64)
+    for _ in range(args.steps):
+        step()
+    times = plan.timing_collect()
+    plan.timing_enable(False)
+    torch.cuda.synchronize()
+
+    alg = algorithmic(spec, info["cascade_members"])
+    per_kernel = {k: {"launches": n, "avg_us": (ms * 1e3 / n) if n else None}
+                  for k, (n, ms) in times.items()}
+    decode_heavy = alg["flops_prefill"] == 0 and spec.dtype == "bf16"
+    if decode_heavy:
+        metric_value = alg["kv_total"] * LAYERS / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+    else:
+        metric_value = alg["flops_total"] * LAYERS / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+    # dominant kernel: the one with the largest summed time
+    dom = max((k for k in times if times[k][0]), key=lambda k: times[k][1])
+    n_l, ms_l = times[dom]
+    avg_s = ms_l / n_l * 1e-3
+    if dom == "prefill":
+        roof = dict(bound="mfma", achieved=alg["flops_prefill"] / avg_s / 1e12,
+                    peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
+    elif dom == "decode":
+        roof = dict(bound="hbm", achieved=alg["kv_decode"] / avg_s / 1e9, peak=PEAK_HBM_GBPS,
+                    unit="GB/s")
+    elif dom == "store":
+        roof = dict(bound="hbm", achieved=alg["store_bytes"] / avg_s / 1e9, peak=PEAK_HBM_GBPS,
+                    unit="GB/s")
+    else:
+        roof = dict(bound="alu", achieved=alg["flops_total"] / avg_s / 1e12, peak=78.6,
+                    unit="TFLOP/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = dom
+    roof["traffic"] = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(spec, layer0, H)
+        cpu.pop("seconds", None)
+        if unit == "GB/s":
+            cpu["note"] = "oracle rate in TFLOP/s of the sampled rows"
+
+    line = {
+        "metric": "attention TFLOP/s (prefill-heavy) and KV-read GB/s (decode-heavy), 1 MI355X",
+        "value": round(metric_value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded N(0,1) tensors, seeded page allocation)",
+        "config": {"workload": desc, "layers_per_step": LAYERS, "pool_sets": npools,
+                   "batch": spec.bs, "tokens": spec.T,
+                   "step": "prepare_metadata + 32 x (store_kv + attend)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": {
+            "per_kernel": per_kernel,
+            "layer_us": round(ms_per_step * 1e3 / LAYERS, 2),
+            "attention_tflops": round(alg["flops_total"] * LAYERS / (ms_per_step * 1e-3) / 1e12, 3),
+            "kv_read_GBps": round(alg["kv_total"] * LAYERS / (ms_per_step * 1e-3) / 1e9, 1),
+            "decode_kernel_GBps": (round(alg["kv_decode"] / (times["decode"][1] / times["decode"][0]
+                                                             * 1e-3) / 1e9, 1)
+                                   if times["decode"][0] else None),
+            "algorithmic_per_layer": alg,
+            "plan": info,
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

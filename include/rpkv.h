@@ -1,0 +1,275 @@
+/*
+ * rpkv.h -- C ABI of the ragged, paged KV-store attention library for MI355X
+ * (gfx950).  One step of one attention layer over a packed batch that mixes
+ * prefill, chunked-prefill and decode requests:
+ *
+ *   1. store_kv: this step's new K/V rows are scattered into the layer's paged
+ *      KV pool by slot;
+ *   2. attend:   the queries of request i, rows [cu_q[i], cu_q[i+1]) of the
+ *      packed q, attend to the first cache_seqlens[i] pool slots named by row i
+ *      of the page table, with a bottom-right causal mask and grouped KV heads.
+ *
+ * Sources (page title, then section):
+ *  - mini-sglang "The attention backend and a reference implementation",
+ *    "The interface": metadata is prepared once per batch and reused by every
+ *    layer; forward(q, k, v, layer) writes the new K/V before reading the pool.
+ *    "Variable-length, paged attention with prefixes": cu_seqlens_q,
+ *    cache_seqlens, page-table rows, the bottom-right mask (query r of n with L
+ *    keys sits at position L-n+r and sees keys 0..L-n+r), GQA head sharing.
+ *  - vLLM "Attention backends: backend, metadata builder and implementation",
+ *    Step 2: the implementation writes into a caller-provided output; the KV
+ *    cache update can be a separate call that scatters by slot_mapping.
+ *    Step 1: a backend answers capability questions (head sizes, dtypes).
+ *  - SGLang source walkthrough "Attention backends", 3.1 (plan once, then run;
+ *    a caller-provided device workspace), 3.3 (cascade: a shared prefix attended
+ *    once and merged with each request's own tail by log-sum-exp), 6 (a mixed
+ *    batch is split by token into decode work and prefill work).
+ *  - "Variable-length batching and one mixed forward pass", exercise 2: pure
+ *    decode work uses split-KV (flash-decoding) kernels; "Source code": the
+ *    logits indices are cu_q[1:] - 1.
+ *
+ * Conventions for every call
+ *  - Device pointers are HIP device memory on the current device; host pointers
+ *    are ordinary host memory.  The library never frees caller memory.
+ *  - A stream argument is a hipStream_t passed as void* (NULL = default stream).
+ *    All device work of a call is enqueued on that stream; no call blocks on the
+ *    device except where stated.  Calls are not thread-safe on one plan.
+ *  - Every call returns an rpkv_status.  On failure nothing is enqueued, no
+ *    caller memory is written, and rpkv_last_error() describes the reason.
+ *  - Layouts (row-major, contiguous):
+ *      q, out          [T, Hq, D]                    T = cu_q[batch]
+ *      k, v (new rows) [T, Hkv, D]
+ *      K pool, V pool  [num_pages, page_size, Hkv, D] for one layer, i.e.
+ *                      [num_slots, Hkv, D] with slot = page * page_size + offset
+ *      page table      [batch, >= cols] int32 page ids, row stride in elements;
+ *                      logical position x of request i lives in slot
+ *                      table[i][x / page_size] * page_size + x % page_size.
+ *    Entries beyond a row's first ceil(L/page_size) are never read.
+ *  - Query head h reads KV head h / (Hq / Hkv).
+ */
+#ifndef RPKV_H
+#define RPKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rpkv_status {
+  RPKV_OK = 0,
+  RPKV_ERR_INVALID_ARG = 1,         /* an argument breaks a documented rule       */
+  RPKV_ERR_UNSUPPORTED = 2,         /* no kernel for this head size/dtype/page    */
+  RPKV_ERR_WORKSPACE_TOO_SMALL = 3, /* see rpkv_workspace_bytes                    */
+  RPKV_ERR_NOT_PREPARED = 4,        /* attend/forward before a successful prepare  */
+  RPKV_ERR_HIP = 5,                 /* the HIP runtime reported an error           */
+  RPKV_ERR_CAPACITY = 6             /* batch exceeds the plan's stated capacities  */
+} rpkv_status;
+
+typedef enum rpkv_dtype {
+  RPKV_BF16 = 0, /* bfloat16 in, fp32 accumulate and softmax, bf16 out (RNE) */
+  RPKV_F32 = 1   /* float32 throughout                                       */
+} rpkv_dtype;
+
+/* Fixed properties of one attention layer type and the plan's capacities.
+ * Zero in a tuning field selects the library default. */
+typedef struct rpkv_shape {
+  int32_t num_q_heads;       /* Hq                                              */
+  int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0 and Hq / Hkv <= 128          */
+  int32_t head_dim;          /* D: 128 (bf16); 64 or 128 (f32)                  */
+  int32_t page_size;         /* tokens per page: a power of two in [1, 1024]    */
+  int32_t dtype;             /* rpkv_dtype of q, k, v, the pools and out        */
+  int32_t max_batch;         /* capacity: requests per batch                    */
+  int64_t num_pages;         /* pages in one layer's pool                       */
+  int64_t max_tokens;        /* capacity: new tokens per batch (T)              */
+  int32_t max_pages_per_req; /* capacity: page-table columns a request may use  */
+  int32_t decode_max_rows;   /* tuning: a request is decode-type iff
+                                n*Hq/Hkv <= this (default 16, at most 16)      */
+  int32_t split_target;      /* tuning: target number of decode work items per
+                                launch when choosing split-KV chunks (default
+                                8192)                                           */
+  int32_t split_min_keys;    /* tuning: smallest split-KV chunk in keys
+                                (default 256; rounded up to 32)                 */
+} rpkv_shape;
+
+/* Cascade hint: requests [first_req, first_req + num_reqs) of the batch have
+ * identical page ids in their first prefix_len / page_size columns
+ * (prefix_len must be a multiple of page_size).  The shared prefix is then read
+ * once for all eligible members and merged with each member's own tail.  A member
+ * is eligible if it is decode-type and none of its new tokens lies in the prefix
+ * (L - n >= prefix_len); other members are computed without the cascade. */
+typedef struct rpkv_prefix_group {
+  int32_t first_req;
+  int32_t num_reqs;
+  int32_t prefix_len;
+} rpkv_prefix_group;
+
+typedef struct rpkv_plan rpkv_plan;
+
+/* What the last successful plan holds (host-side summary). */
+typedef struct rpkv_plan_info {
+  int32_t batch;
+  int32_t num_tokens;          /* T                                       */
+  int32_t max_seqlen_q;
+  int32_t max_seqlen_k;
+  int32_t num_prefill_items;   /* MFMA tiles, incl. cascade prefix tiles  */
+  int32_t num_decode_items;    /* split-KV chunks (one wave each)         */
+  int32_t num_cascade_items;   /* of which shared-prefix tiles            */
+  int32_t num_merge_tokens;    /* tokens whose heads are merged           */
+  int64_t num_partials;        /* partial results (token x split)         */
+  int64_t workspace_bytes;     /* device workspace the batch needs        */
+  int32_t decode_chunk;        /* split-KV chunk in keys                  */
+  int32_t cascade_members;     /* requests served through the cascade     */
+  double plan_host_us;         /* host time of the last plan              */
+} rpkv_plan_info;
+
+/* Kernel timing (benchmarks): per kernel kind, launches and summed durations
+ * measured with HIP events recorded on the launch stream around each launch. */
+typedef enum rpkv_kernel_kind {
+  RPKV_KERNEL_STORE = 0,
+  RPKV_KERNEL_PREFILL = 1, /* bf16 MFMA tiles, incl. cascade prefix */
+  RPKV_KERNEL_DECODE = 2,  /* bf16 split-KV                         */
+  RPKV_KERNEL_MERGE = 3,   /* log-sum-exp merge                     */
+  RPKV_KERNEL_F32 = 4,     /* fp32 tiles                            */
+  RPKV_KERNEL_KINDS = 5
+} rpkv_kernel_kind;
+
+typedef struct rpkv_kernel_times {
+  int64_t launches[8];
+  double total_ms[8];
+} rpkv_kernel_times;
+
+/* ---------------------------------------------------------------- errors */
+
+/* Static, human-readable name of a status. */
+const char *rpkv_status_string(rpkv_status status);
+
+/* Message of the last failed call made on this thread ("" if none).  The
+ * pointer stays valid until the next call on this thread. */
+const char *rpkv_last_error(void);
+
+/* ------------------------------------------------------------- plan setup */
+
+/* Capability query (vLLM Step 1): RPKV_OK if a plan can be made for this
+ * shape, else RPKV_ERR_UNSUPPORTED or RPKV_ERR_INVALID_ARG.  No device work. */
+rpkv_status rpkv_supports(const rpkv_shape *shape);
+
+/* Create a plan for one layer type.  Host-only: allocates host memory; device
+ * buffers are allocated by the first rpkv_prepare_metadata.  *out receives the
+ * plan, owned by the library until rpkv_plan_destroy. */
+rpkv_status rpkv_plan_create(const rpkv_shape *shape, rpkv_plan **out);
+
+/* Release a plan and its device buffers (waits for the device). NULL is a no-op. */
+void rpkv_plan_destroy(rpkv_plan *plan);
+
+/* --------------------------------------------------------- once per batch */
+
+/* Host half of prepare_metadata: validate the batch and build the work
+ * partition (classification into decode-type and prefill-type requests, MFMA
+ * tiles, split-KV chunks, cascade tiles, partial-result layout, merge list).
+ * No device work; usable without a GPU.
+ *   batch              requests, 0 <= batch <= max_batch
+ *   cu_seqlens_q_host  [batch+1] host, cu[0] = 0, non-decreasing, cu[batch] <=
+ *                      max_tokens; n_i = cu[i+1]-cu[i]
+ *   cache_seqlens_host [batch] host, L_i >= n_i (KV length including this step)
+ *   page_table_cols    columns readable in each page-table row; needs
+ *                      ceil(L_i / page_size) <= cols <= max_pages_per_req
+ *   page_table_host    optional host copy [batch, cols] (row stride = cols); when
+ *                      given, page ids are checked to be in [0, num_pages) and
+ *                      cascade hints are checked against it
+ *   groups_host        optional cascade hints [num_groups]
+ * Errors: INVALID_ARG (rule broken), CAPACITY (capacities exceeded). */
+rpkv_status rpkv_plan_batch(rpkv_plan *plan, int32_t batch, const int32_t *cu_seqlens_q_host,
+                            const int32_t *cache_seqlens_host, int32_t page_table_cols,
+                            const int32_t *page_table_host, const rpkv_prefix_group *groups_host,
+                            int32_t num_groups);
+
+/* prepare_metadata (once per batch, reused by every layer): rpkv_plan_batch,
+ * then one asynchronous host-to-device copy of the work partition on `stream`.
+ *   page_table_dev     device [batch, stride] int32; must stay valid and
+ *                      unchanged while attend/forward of this batch run
+ *   page_table_stride  elements between rows (>= page_table_cols)
+ *   workspace_dev      caller-owned device scratch for split-KV / cascade
+ *                      partials, 256-byte aligned; may be NULL when the batch
+ *                      needs none.  If it is smaller than the batch needs, the
+ *                      call fails with WORKSPACE_TOO_SMALL and
+ *                      rpkv_workspace_bytes reports the size to provide.
+ * The host arrays may be reused by the caller as soon as the call returns.
+ * Page ids outside [0, num_pages) that reach a kernel are clamped (results
+ * unspecified, no out-of-bounds access). */
+rpkv_status rpkv_prepare_metadata(rpkv_plan *plan, int32_t batch, const int32_t *cu_seqlens_q_host,
+                                  const int32_t *cache_seqlens_host, const int32_t *page_table_dev,
+                                  int64_t page_table_stride, int32_t page_table_cols,
+                                  const int32_t *page_table_host,
+                                  const rpkv_prefix_group *groups_host, int32_t num_groups,
+                                  void *workspace_dev, size_t workspace_bytes, void *stream);
+
+/* Device workspace bytes the last planned batch needs (0 if none). */
+rpkv_status rpkv_workspace_bytes(const rpkv_plan *plan, size_t *bytes);
+
+/* get_last_indices: out_host[i] = cu_q[i+1] - 1 for the planned batch, or -1
+ * for a request with no queries.  out_host has room for `batch` entries. */
+rpkv_status rpkv_last_indices(const rpkv_plan *plan, int32_t *out_host);
+
+/* Summary of the last planned batch. */
+rpkv_status rpkv_plan_get_info(const rpkv_plan *plan, rpkv_plan_info *info);
+
+/* Host copy of the last plan's work items for inspection: kind 0 = prefill
+ * tiles, 1 = decode chunks.  Each item is 8 int32: request, KV head, first
+ * token (or cascade token-list offset), token count, position of the first
+ * token (-1 for a cascade prefix tile), key begin, key end, split index (-1 =
+ * final output).  Padding items (token count 0) are included.  Writes
+ * min(capacity, count) items; *count receives the total. */
+rpkv_status rpkv_plan_get_items(const rpkv_plan *plan, int32_t kind, int32_t *items_host,
+                                int32_t capacity, int32_t *count);
+
+/* Host copy of the cascade token list (token ids of each cascade prefix tile,
+ * addressed by the tile's token-list offset). */
+rpkv_status rpkv_plan_get_token_list(const rpkv_plan *plan, int32_t *out_host, int32_t capacity,
+                                     int32_t *count);
+
+/* ---------------------------------------------------------- once per layer */
+
+/* store_kv / do_kv_cache_update: for t < num_tokens, K pool row slot_mapping[t]
+ * = k[t] and V pool row slot_mapping[t] = v[t], bit for bit.  A negative slot
+ * is a padding token and writes nothing; a slot >= num_pages*page_size is
+ * skipped (never written).  Slots must be distinct (duplicates race).  Uses only
+ * the plan's shape; does not need a prepared batch.
+ *   k, v          device [num_tokens, Hkv, D]
+ *   slot_mapping  device int32 [num_tokens]
+ *   k_pool/v_pool device [num_pages*page_size, Hkv, D] of one layer */
+rpkv_status rpkv_store_kv(rpkv_plan *plan, const void *k, const void *v,
+                          const int32_t *slot_mapping, int64_t num_tokens, void *k_pool,
+                          void *v_pool, void *stream);
+
+/* attend: out[t, h, :] = softmax over the visible keys of request i(t) of
+ * scale * <q[t,h,:], K[.]> applied to V, for every token of the prepared batch.
+ * Must be enqueued after this layer's store_kv (same stream order).
+ *   q     device [T, Hq, D];  out device [T, Hq, D], caller-allocated, must not
+ *         alias q or the pools;  scale usually 1/sqrt(D), finite and > 0. */
+rpkv_status rpkv_attend(rpkv_plan *plan, const void *q, const void *k_pool, const void *v_pool,
+                        void *out, float scale, void *stream);
+
+/* forward(q, k, v, layer): rpkv_store_kv of the batch's T tokens, then
+ * rpkv_attend, on one stream (write first, then read).  The layer is chosen by
+ * the pool pointers passed. */
+rpkv_status rpkv_forward(rpkv_plan *plan, const void *q, const void *k, const void *v,
+                         const int32_t *slot_mapping, void *k_pool, void *v_pool, void *out,
+                         float scale, void *stream);
+
+/* ------------------------------------------------------- instrumentation */
+
+/* Enable (1) or disable (0) per-launch HIP-event timing on this plan, with room
+ * for max_launches launches before rpkv_timing_collect must be called. */
+rpkv_status rpkv_timing_enable(rpkv_plan *plan, int32_t enable, int32_t max_launches);
+
+/* Wait for the recorded events, add their durations into *out and reset the
+ * record.  Blocks the host until the recorded launches finish. */
+rpkv_status rpkv_timing_collect(rpkv_plan *plan, rpkv_kernel_times *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RPKV_H */

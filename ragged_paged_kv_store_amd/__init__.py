@@ -1,0 +1,276 @@
+"""Python binding of librpkv.so (include/rpkv.h): argument marshalling only.
+
+Every step of the path (planning, store_kv, attention tiles, split-KV chunks,
+the merge) runs in the native library; this module converts torch tensors and
+numpy arrays into pointers and sizes, keeps the caller's workspace large enough,
+and raises on any non-OK status.  There is no fallback: if the built library is
+missing, importing the package raises.
+
+Layouts are those of the C header: q/out [T, Hq, D]; k/v [T, Hkv, D]; one
+layer's pools [num_pages * page_size, Hkv, D]; page table [batch, cols] int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "librpkv.so")
+
+RPKV_OK = 0
+STATUS = {0: "RPKV_OK", 1: "RPKV_ERR_INVALID_ARG", 2: "RPKV_ERR_UNSUPPORTED",
+          3: "RPKV_ERR_WORKSPACE_TOO_SMALL", 4: "RPKV_ERR_NOT_PREPARED", 5: "RPKV_ERR_HIP",
+          6: "RPKV_ERR_CAPACITY"}
+BF16, F32 = 0, 1
+KERNEL_KINDS = ("store", "prefill", "decode", "merge", "f32")
+
+# every function include/rpkv.h declares
+EXPORTS = (
+    "rpkv_status_string", "rpkv_last_error", "rpkv_supports", "rpkv_plan_create",
+    "rpkv_plan_destroy", "rpkv_plan_batch", "rpkv_prepare_metadata", "rpkv_workspace_bytes",
+    "rpkv_last_indices", "rpkv_plan_get_info", "rpkv_plan_get_items", "rpkv_plan_get_token_list",
+    "rpkv_store_kv", "rpkv_attend", "rpkv_forward", "rpkv_timing_enable", "rpkv_timing_collect",
+)
+
+
+class RpkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64), ("max_tokens", ctypes.c_int64),
+                ("max_pages_per_req", ctypes.c_int32), ("decode_max_rows", ctypes.c_int32),
+                ("split_target", ctypes.c_int32), ("split_min_keys", ctypes.c_int32)]
+
+
+class PrefixGroup(ctypes.Structure):
+    _fields_ = [("first_req", ctypes.c_int32), ("num_reqs", ctypes.c_int32),
+                ("prefix_len", ctypes.c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
+                ("num_prefill_items", ctypes.c_int32), ("num_decode_items", ctypes.c_int32),
+                ("num_cascade_items", ctypes.c_int32), ("num_merge_tokens", ctypes.c_int32),
+                ("num_partials", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("decode_chunk", ctypes.c_int32), ("cascade_members", ctypes.c_int32),
+                ("plan_host_us", ctypes.c_double)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class KernelTimes(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64 * 8), ("total_ms", ctypes.c_double * 8)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python -m ragged_paged_kv_store_amd.build_lib")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    P = ctypes.POINTER
+    sigs = {
+        "rpkv_status_string": (ctypes.c_char_p, [i32]),
+        "rpkv_last_error": (ctypes.c_char_p, []),
+        "rpkv_supports": (i32, [P(Shape)]),
+        "rpkv_plan_create": (i32, [P(Shape), P(vp)]),
+        "rpkv_plan_destroy": (None, [vp]),
+        "rpkv_plan_batch": (i32, [vp, i32, vp, vp, i32, vp, vp, i32]),
+        "rpkv_prepare_metadata": (i32, [vp, i32, vp, vp, vp, i64, i32, vp, vp, i32, vp, sz, vp]),
+        "rpkv_workspace_bytes": (i32, [vp, P(sz)]),
+        "rpkv_last_indices": (i32, [vp, vp]),
+        "rpkv_plan_get_info": (i32, [vp, P(PlanInfo)]),
+        "rpkv_plan_get_items": (i32, [vp, i32, vp, i32, P(i32)]),
+        "rpkv_plan_get_token_list": (i32, [vp, vp, i32, P(i32)]),
+        "rpkv_store_kv": (i32, [vp, vp, vp, vp, i64, vp, vp, vp]),
+        "rpkv_attend": (i32, [vp, vp, vp, vp, vp, ctypes.c_float, vp]),
+        "rpkv_forward": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp]),
+        "rpkv_timing_enable": (i32, [vp, i32, i32]),
+        "rpkv_timing_collect": (i32, [vp, P(KernelTimes)]),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def _check(st: int) -> None:
+    if st != RPKV_OK:
+        raise RpkvError(st, lib.rpkv_last_error().decode())
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+def _ptr(t) -> Optional[int]:
+    """Device/host pointer of a torch tensor (or None)."""
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def supports(**kw) -> Tuple[bool, str]:
+    s = make_shape(**kw)
+    st = lib.rpkv_supports(ctypes.byref(s))
+    return st == RPKV_OK, ("" if st == RPKV_OK else lib.rpkv_last_error().decode())
+
+
+def make_shape(num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int, dtype: int,
+               max_batch: int, num_pages: int, max_tokens: int, max_pages_per_req: int,
+               decode_max_rows: int = 0, split_target: int = 0, split_min_keys: int = 0) -> Shape:
+    return Shape(num_q_heads, num_kv_heads, head_dim, page_size, dtype, max_batch, num_pages,
+                 max_tokens, max_pages_per_req, decode_max_rows, split_target, split_min_keys)
+
+
+class Plan:
+    """One layer type's plan: prepare once per batch, then store/attend per layer."""
+
+    def __init__(self, **shape_kw):
+        self.shape = make_shape(**shape_kw)
+        h = ctypes.c_void_p()
+        _check(lib.rpkv_plan_create(ctypes.byref(self.shape), ctypes.byref(h)))
+        self._h = h
+        self.workspace = None      # torch uint8 device tensor, grown on demand
+        self._pt = None            # keep the page table alive while prepared
+        self.batch = 0
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib.rpkv_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------ per batch
+    def plan_host(self, cu_q, cache_seqlens, page_table_cols: int, page_table_host=None,
+                  groups: Sequence[Tuple[int, int, int]] = ()):
+        """Host-only planning (no device work)."""
+        cu = _i32(cu_q)
+        sl = _i32(cache_seqlens)
+        bs = len(sl)
+        pth = None if page_table_host is None else _i32(page_table_host)
+        if pth is not None:
+            assert pth.shape == (bs, page_table_cols)
+        garr = (PrefixGroup * max(len(groups), 1))(*[PrefixGroup(*g) for g in groups])
+        _check(lib.rpkv_plan_batch(self._h, bs, cu.ctypes.data, sl.ctypes.data, page_table_cols,
+                                   None if pth is None else pth.ctypes.data,
+                                   ctypes.cast(garr, ctypes.c_void_p) if groups else None,
+                                   len(groups)))
+        self.batch = bs
+
+    def prepare(self, cu_q, cache_seqlens, page_table, page_table_host=None,
+                groups: Sequence[Tuple[int, int, int]] = (), stream=None):
+        """prepare_metadata: plan on the host and upload the work partition.
+
+        page_table: torch int32 device tensor [batch, cols] (row stride = its
+        stride(0)).  The workspace is (re)allocated with torch when too small.
+        """
+        import torch
+        cu = _i32(cu_q)
+        sl = _i32(cache_seqlens)
+        bs = len(sl)
+        assert page_table.dtype == torch.int32 and page_table.dim() == 2
+        assert page_table.stride(1) == 1
+        cols = page_table.shape[1]
+        pth = None if page_table_host is None else _i32(page_table_host)
+        garr = (PrefixGroup * max(len(groups), 1))(*[PrefixGroup(*g) for g in groups])
+        gptr = ctypes.cast(garr, ctypes.c_void_p) if groups else None
+        s = _stream(stream)
+        for _ in range(2):
+            ws = self.workspace
+            st = lib.rpkv_prepare_metadata(
+                self._h, bs, cu.ctypes.data, sl.ctypes.data, page_table.data_ptr(),
+                page_table.stride(0), cols, None if pth is None else pth.ctypes.data, gptr,
+                len(groups), None if ws is None else ws.data_ptr(),
+                0 if ws is None else ws.numel(), s)
+            if st == 3:  # workspace too small: grow and plan again
+                need = ctypes.c_size_t()
+                _check(lib.rpkv_workspace_bytes(self._h, ctypes.byref(need)))
+                self.workspace = torch.empty(int(need.value * 1.25) + 256, dtype=torch.uint8,
+                                             device=page_table.device)
+                continue
+            _check(st)
+            break
+        self._pt = page_table
+        self.batch = bs
+
+    def info(self) -> dict:
+        inf = PlanInfo()
+        _check(lib.rpkv_plan_get_info(self._h, ctypes.byref(inf)))
+        return inf.as_dict()
+
+    def items(self, kind: int) -> np.ndarray:
+        n = ctypes.c_int32()
+        _check(lib.rpkv_plan_get_items(self._h, kind, None, 0, ctypes.byref(n)))
+        out = np.zeros((max(n.value, 1), 8), np.int32)
+        _check(lib.rpkv_plan_get_items(self._h, kind, out.ctypes.data, n.value, ctypes.byref(n)))
+        return out[:n.value]
+
+    def token_list(self) -> np.ndarray:
+        n = ctypes.c_int32()
+        _check(lib.rpkv_plan_get_token_list(self._h, None, 0, ctypes.byref(n)))
+        out = np.zeros(max(n.value, 1), np.int32)
+        _check(lib.rpkv_plan_get_token_list(self._h, out.ctypes.data, n.value, ctypes.byref(n)))
+        return out[:n.value]
+
+    def last_indices(self) -> np.ndarray:
+        out = np.zeros(max(self.batch, 1), np.int32)
+        _check(lib.rpkv_last_indices(self._h, out.ctypes.data))
+        return out[:self.batch]
+
+    def workspace_bytes(self) -> int:
+        need = ctypes.c_size_t()
+        _check(lib.rpkv_workspace_bytes(self._h, ctypes.byref(need)))
+        return int(need.value)
+
+    # ------------------------------------------------------------ per layer
+    def store_kv(self, k, v, slot_mapping, k_pool, v_pool, stream=None):
+        _check(lib.rpkv_store_kv(self._h, _ptr(k), _ptr(v), _ptr(slot_mapping),
+                                 int(slot_mapping.numel()) if slot_mapping is not None else 0,
+                                 _ptr(k_pool), _ptr(v_pool), _stream(stream)))
+
+    def attend(self, q, k_pool, v_pool, out, scale: float, stream=None):
+        _check(lib.rpkv_attend(self._h, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out),
+                               float(scale), _stream(stream)))
+
+    def forward(self, q, k, v, slot_mapping, k_pool, v_pool, out, scale: float, stream=None):
+        _check(lib.rpkv_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(slot_mapping),
+                                _ptr(k_pool), _ptr(v_pool), _ptr(out), float(scale),
+                                _stream(stream)))
+
+    # ------------------------------------------------------- instrumentation
+    def timing_enable(self, enable: bool, max_launches: int = 4096):
+        _check(lib.rpkv_timing_enable(self._h, 1 if enable else 0, max_launches))
+
+    def timing_collect(self) -> dict:
+        kt = KernelTimes()
+        _check(lib.rpkv_timing_collect(self._h, ctypes.byref(kt)))
+        return {name: (int(kt.launches[i]), float(kt.total_ms[i]))
+                for i, name in enumerate(KERNEL_KINDS)}

@@ -1,0 +1,449 @@
+// C ABI (include/rpkv.h): argument checks, per-batch metadata upload and the
+// per-layer launch sequence store_kv -> tiles -> split-KV chunks -> merge.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "rpkv_internal.h"
+
+using rpkv::HostPlan;
+using rpkv::Item;
+using rpkv::Shape;
+
+namespace {
+thread_local std::string g_err;
+
+rpkv_status fail(rpkv_status st, const std::string &msg) {
+  g_err = msg;
+  return st;
+}
+
+rpkv_status hip_fail(int err, const char *what) {
+  return fail(RPKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString((hipError_t)err));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+}  // namespace
+
+struct rpkv_plan {
+  Shape s{};
+  HostPlan hp;
+  bool planned = false;
+  bool prepared = false;
+  int device = -1;
+  // device copy of the work partition
+  char *dmeta = nullptr;
+  size_t dmeta_cap = 0;
+  size_t off_pre = 0, off_dec = 0, off_pbase = 0, off_merge = 0, off_tok = 0, meta_bytes = 0;
+  // pinned staging, two buffers so a new batch never overwrites one in flight
+  char *hmeta[2] = {nullptr, nullptr};
+  size_t hmeta_cap[2] = {0, 0};
+  hipEvent_t hev[2] = {nullptr, nullptr};
+  bool hev_live[2] = {false, false};
+  int hcur = 0;
+  // bound per batch
+  const int32_t *page_table = nullptr;
+  int64_t pt_stride = 0;
+  float *o_part = nullptr;
+  float *lse_part = nullptr;
+  size_t ws_need = 0;
+  // timing
+  bool timing = false;
+  int32_t max_launches = 0;
+  std::vector<hipEvent_t> ev;
+  std::vector<int32_t> ev_kind;
+  int32_t n_rec = 0;
+};
+
+namespace {
+
+size_t workspace_need(const rpkv_plan *p) {
+  if (p->hp.n_partials == 0) return 0;
+  const size_t rows = (size_t)p->hp.n_partials * p->s.Hq;
+  return align256(rows * p->s.D * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+template <class F>
+rpkv_status timed(rpkv_plan *p, int kind, void *stream, F &&launch, const char *what) {
+  const bool rec = p->timing && p->n_rec < p->max_launches;
+  if (rec) {
+    int e = hipEventRecord(p->ev[2 * p->n_rec], (hipStream_t)stream);
+    if (e) return hip_fail(e, "hipEventRecord");
+  }
+  int err = launch();
+  if (err) return hip_fail(err, what);
+  if (rec) {
+    int e = hipEventRecord(p->ev[2 * p->n_rec + 1], (hipStream_t)stream);
+    if (e) return hip_fail(e, "hipEventRecord");
+    p->ev_kind[p->n_rec++] = kind;
+  }
+  return RPKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rpkv_status_string(rpkv_status st) {
+  switch (st) {
+    case RPKV_OK: return "RPKV_OK";
+    case RPKV_ERR_INVALID_ARG: return "RPKV_ERR_INVALID_ARG";
+    case RPKV_ERR_UNSUPPORTED: return "RPKV_ERR_UNSUPPORTED";
+    case RPKV_ERR_WORKSPACE_TOO_SMALL: return "RPKV_ERR_WORKSPACE_TOO_SMALL";
+    case RPKV_ERR_NOT_PREPARED: return "RPKV_ERR_NOT_PREPARED";
+    case RPKV_ERR_HIP: return "RPKV_ERR_HIP";
+    case RPKV_ERR_CAPACITY: return "RPKV_ERR_CAPACITY";
+  }
+  return "RPKV_ERR_UNKNOWN";
+}
+
+const char *rpkv_last_error(void) { return g_err.c_str(); }
+
+rpkv_status rpkv_supports(const rpkv_shape *shape) {
+  Shape s;
+  std::string msg;
+  rpkv_status st = rpkv::check_shape(shape, &s, &msg);
+  if (st != RPKV_OK) return fail(st, msg);
+  return RPKV_OK;
+}
+
+rpkv_status rpkv_plan_create(const rpkv_shape *shape, rpkv_plan **out) {
+  if (!out) return fail(RPKV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  Shape s;
+  std::string msg;
+  rpkv_status st = rpkv::check_shape(shape, &s, &msg);
+  if (st != RPKV_OK) return fail(st, msg);
+  rpkv_plan *p = new (std::nothrow) rpkv_plan();
+  if (!p) return fail(RPKV_ERR_CAPACITY, "host allocation failed");
+  p->s = s;
+  *out = p;
+  return RPKV_OK;
+}
+
+void rpkv_plan_destroy(rpkv_plan *p) {
+  if (!p) return;
+  if (p->dmeta || p->hmeta[0] || p->hmeta[1] || !p->ev.empty()) {
+    if (p->device >= 0) (void)hipSetDevice(p->device);
+    (void)hipDeviceSynchronize();
+  }
+  if (p->dmeta) (void)hipFree(p->dmeta);
+  for (int i = 0; i < 2; ++i) {
+    if (p->hmeta[i]) (void)hipHostFree(p->hmeta[i]);
+    if (p->hev[i]) (void)hipEventDestroy(p->hev[i]);
+  }
+  for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
+  delete p;
+}
+
+rpkv_status rpkv_plan_batch(rpkv_plan *p, int32_t batch, const int32_t *cu, const int32_t *seqlens,
+                            int32_t cols, const int32_t *pt_host, const rpkv_prefix_group *groups,
+                            int32_t ngroups) {
+  if (!p) return fail(RPKV_ERR_INVALID_ARG, "plan is NULL");
+  p->prepared = false;
+  p->planned = false;
+  std::string msg;
+  rpkv_status st;
+  try {
+    st = rpkv::plan_batch_host(p->s, batch, cu, seqlens, cols, pt_host, groups, ngroups, &p->hp,
+                               &msg);
+  } catch (const std::bad_alloc &) {
+    return fail(RPKV_ERR_CAPACITY, "host allocation failed while planning");
+  }
+  if (st != RPKV_OK) return fail(st, msg);
+  p->planned = true;
+  p->ws_need = workspace_need(p);
+  return RPKV_OK;
+}
+
+rpkv_status rpkv_prepare_metadata(rpkv_plan *p, int32_t batch, const int32_t *cu,
+                                  const int32_t *seqlens, const int32_t *pt_dev, int64_t pt_stride,
+                                  int32_t cols, const int32_t *pt_host,
+                                  const rpkv_prefix_group *groups, int32_t ngroups, void *ws,
+                                  size_t ws_bytes, void *stream) {
+  if (!p) return fail(RPKV_ERR_INVALID_ARG, "plan is NULL");
+  if (pt_stride < cols) return fail(RPKV_ERR_INVALID_ARG, "page_table_stride < page_table_cols");
+  rpkv_status st = rpkv_plan_batch(p, batch, cu, seqlens, cols, pt_host, groups, ngroups);
+  if (st != RPKV_OK) return st;
+  p->planned = false;  // becomes usable only once uploaded
+  const HostPlan &hp = p->hp;
+  bool any_keys = false;
+  for (int32_t i = 0; i < batch; ++i) any_keys |= seqlens[i] > 0 && cu[i + 1] > cu[i];
+  if (any_keys && !pt_dev) return fail(RPKV_ERR_INVALID_ARG, "page_table_dev is NULL");
+  if (p->ws_need > 0) {
+    if (!ws || ws_bytes < p->ws_need)
+      return fail(RPKV_ERR_WORKSPACE_TOO_SMALL,
+                  "workspace of " + std::to_string(p->ws_need) + " bytes needed, " +
+                      std::to_string(ws ? ws_bytes : 0) + " given");
+    if ((uintptr_t)ws & 255) return fail(RPKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
+  int dev = 0;
+  int e = hipGetDevice(&dev);
+  if (e) return hip_fail(e, "hipGetDevice");
+  if (p->device >= 0 && p->device != dev)
+    return fail(RPKV_ERR_INVALID_ARG, "a plan is bound to the device of its first prepare");
+
+  // layout of the device copy
+  size_t off = 0;
+  p->off_pre = off;
+  off = align256(off + hp.prefill.size() * sizeof(Item));
+  p->off_dec = off;
+  off = align256(off + hp.decode.size() * sizeof(Item));
+  p->off_pbase = off;
+  off = align256(off + hp.tok_pbase.size() * sizeof(int32_t));
+  p->off_merge = off;
+  off = align256(off + hp.merge.size() * sizeof(int32_t));
+  p->off_tok = off;
+  off = align256(off + hp.toklist.size() * sizeof(int32_t));
+  const size_t bytes = std::max<size_t>(off, 256);
+
+  if (bytes > p->dmeta_cap) {
+    if (p->dmeta) {
+      e = hipStreamSynchronize((hipStream_t)stream);
+      if (e) return hip_fail(e, "hipStreamSynchronize");
+      e = hipFree(p->dmeta);
+      p->dmeta = nullptr;
+      p->dmeta_cap = 0;
+      if (e) return hip_fail(e, "hipFree");
+    }
+    const size_t cap = std::max(bytes, size_t(1) << 16);
+    e = hipMalloc((void **)&p->dmeta, cap);
+    if (e) return hip_fail(e, "hipMalloc (plan metadata)");
+    p->dmeta_cap = cap;
+  }
+  const int c = p->hcur;
+  if (!p->hev[c]) {
+    e = hipEventCreateWithFlags(&p->hev[c], hipEventDisableTiming);
+    if (e) return hip_fail(e, "hipEventCreate");
+  }
+  if (p->hev_live[c]) {
+    e = hipEventSynchronize(p->hev[c]);
+    if (e) return hip_fail(e, "hipEventSynchronize");
+    p->hev_live[c] = false;
+  }
+  if (bytes > p->hmeta_cap[c]) {
+    if (p->hmeta[c]) (void)hipHostFree(p->hmeta[c]);
+    p->hmeta[c] = nullptr;
+    p->hmeta_cap[c] = 0;
+    const size_t cap = std::max(bytes, size_t(1) << 16);
+    e = hipHostMalloc((void **)&p->hmeta[c], cap, hipHostMallocDefault);
+    if (e) return hip_fail(e, "hipHostMalloc (staging)");
+    p->hmeta_cap[c] = cap;
+  }
+  char *h = p->hmeta[c];
+  std::memset(h, 0, bytes);
+  if (!hp.prefill.empty()) std::memcpy(h + p->off_pre, hp.prefill.data(), hp.prefill.size() * sizeof(Item));
+  if (!hp.decode.empty()) std::memcpy(h + p->off_dec, hp.decode.data(), hp.decode.size() * sizeof(Item));
+  if (!hp.tok_pbase.empty())
+    std::memcpy(h + p->off_pbase, hp.tok_pbase.data(), hp.tok_pbase.size() * sizeof(int32_t));
+  if (!hp.merge.empty()) std::memcpy(h + p->off_merge, hp.merge.data(), hp.merge.size() * sizeof(int32_t));
+  if (!hp.toklist.empty())
+    std::memcpy(h + p->off_tok, hp.toklist.data(), hp.toklist.size() * sizeof(int32_t));
+  e = hipMemcpyAsync(p->dmeta, h, bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
+  if (e) return hip_fail(e, "hipMemcpyAsync (metadata)");
+  e = hipEventRecord(p->hev[c], (hipStream_t)stream);
+  if (e) return hip_fail(e, "hipEventRecord");
+  p->hev_live[c] = true;
+  p->hcur ^= 1;
+  p->meta_bytes = bytes;
+  p->device = dev;
+  p->page_table = pt_dev;
+  p->pt_stride = pt_stride;
+  if (p->ws_need > 0) {
+    const size_t rows = (size_t)hp.n_partials * p->s.Hq;
+    p->o_part = (float *)ws;
+    p->lse_part = (float *)((char *)ws + align256(rows * p->s.D * sizeof(float)));
+  } else {
+    p->o_part = p->lse_part = nullptr;
+  }
+  p->planned = true;
+  p->prepared = true;
+  return RPKV_OK;
+}
+
+rpkv_status rpkv_workspace_bytes(const rpkv_plan *p, size_t *bytes) {
+  if (!p || !bytes) return fail(RPKV_ERR_INVALID_ARG, "plan or bytes is NULL");
+  *bytes = p->ws_need;
+  return RPKV_OK;
+}
+
+rpkv_status rpkv_last_indices(const rpkv_plan *p, int32_t *out) {
+  if (!p || !out) return fail(RPKV_ERR_INVALID_ARG, "plan or out is NULL");
+  if (!p->planned) return fail(RPKV_ERR_NOT_PREPARED, "no planned batch");
+  for (int32_t i = 0; i < p->hp.batch; ++i)
+    out[i] = p->hp.cu_q[i + 1] > p->hp.cu_q[i] ? p->hp.cu_q[i + 1] - 1 : -1;
+  return RPKV_OK;
+}
+
+rpkv_status rpkv_plan_get_info(const rpkv_plan *p, rpkv_plan_info *info) {
+  if (!p || !info) return fail(RPKV_ERR_INVALID_ARG, "plan or info is NULL");
+  if (!p->planned) return fail(RPKV_ERR_NOT_PREPARED, "no planned batch");
+  const HostPlan &hp = p->hp;
+  info->batch = hp.batch;
+  info->num_tokens = hp.T;
+  info->max_seqlen_q = hp.max_q;
+  info->max_seqlen_k = hp.max_k;
+  info->num_prefill_items = hp.n_prefill_real;
+  info->num_decode_items = (int32_t)hp.decode.size();
+  info->num_cascade_items = hp.n_cascade_items;
+  info->num_merge_tokens = (int32_t)(hp.merge.size() / 3);
+  info->num_partials = hp.n_partials;
+  info->workspace_bytes = (int64_t)p->ws_need;
+  info->decode_chunk = hp.decode_chunk;
+  info->cascade_members = hp.cascade_members;
+  info->plan_host_us = hp.plan_us;
+  return RPKV_OK;
+}
+
+rpkv_status rpkv_plan_get_items(const rpkv_plan *p, int32_t kind, int32_t *items, int32_t capacity,
+                                int32_t *count) {
+  if (!p || !count || (kind != 0 && kind != 1) || capacity < 0 || (capacity > 0 && !items))
+    return fail(RPKV_ERR_INVALID_ARG, "bad arguments to rpkv_plan_get_items");
+  if (!p->planned) return fail(RPKV_ERR_NOT_PREPARED, "no planned batch");
+  const std::vector<Item> &v = kind == 0 ? p->hp.prefill : p->hp.decode;
+  *count = (int32_t)v.size();
+  const int32_t n = std::min<int32_t>(capacity, (int32_t)v.size());
+  if (n > 0) std::memcpy(items, v.data(), (size_t)n * sizeof(Item));
+  return RPKV_OK;
+}
+
+rpkv_status rpkv_plan_get_token_list(const rpkv_plan *p, int32_t *out, int32_t capacity,
+                                     int32_t *count) {
+  if (!p || !count || capacity < 0 || (capacity > 0 && !out))
+    return fail(RPKV_ERR_INVALID_ARG, "bad arguments to rpkv_plan_get_token_list");
+  if (!p->planned) return fail(RPKV_ERR_NOT_PREPARED, "no planned batch");
+  *count = (int32_t)p->hp.toklist.size();
+  const int32_t n = std::min<int32_t>(capacity, *count);
+  if (n > 0) std::memcpy(out, p->hp.toklist.data(), (size_t)n * sizeof(int32_t));
+  return RPKV_OK;
+}
+
+rpkv_status rpkv_store_kv(rpkv_plan *p, const void *k, const void *v, const int32_t *slots,
+                          int64_t T, void *kpool, void *vpool, void *stream) {
+  if (!p) return fail(RPKV_ERR_INVALID_ARG, "plan is NULL");
+  if (T < 0) return fail(RPKV_ERR_INVALID_ARG, "num_tokens < 0");
+  if (T == 0) return RPKV_OK;
+  if (!k || !v || !slots || !kpool || !vpool)
+    return fail(RPKV_ERR_INVALID_ARG, "k, v, slot_mapping and pools must be non-NULL");
+  if (((uintptr_t)k | (uintptr_t)v | (uintptr_t)kpool | (uintptr_t)vpool) & 15)
+    return fail(RPKV_ERR_INVALID_ARG, "k, v and pools must be 16-byte aligned");
+  const int64_t row_bytes = (int64_t)p->s.Hkv * p->s.D * (p->s.dtype == RPKV_BF16 ? 2 : 4);
+  const int64_t num_slots = p->s.num_pages * p->s.P;
+  return timed(p, RPKV_KERNEL_STORE, stream, [&] {
+    return rpkv::launch_store_kv(k, v, slots, T, row_bytes, num_slots, kpool, vpool, stream);
+  }, "store_kv launch");
+}
+
+rpkv_status rpkv_attend(rpkv_plan *p, const void *q, const void *kpool, const void *vpool,
+                        void *out, float scale, void *stream) {
+  if (!p) return fail(RPKV_ERR_INVALID_ARG, "plan is NULL");
+  if (!p->prepared) return fail(RPKV_ERR_NOT_PREPARED, "attend before a successful prepare_metadata");
+  const HostPlan &hp = p->hp;
+  if (hp.T == 0) return RPKV_OK;
+  if (!q || !kpool || !vpool || !out)
+    return fail(RPKV_ERR_INVALID_ARG, "q, pools and out must be non-NULL");
+  if (((uintptr_t)q | (uintptr_t)kpool | (uintptr_t)vpool | (uintptr_t)out) & 15)
+    return fail(RPKV_ERR_INVALID_ARG, "q, pools and out must be 16-byte aligned");
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(RPKV_ERR_INVALID_ARG, "scale must be finite and positive");
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev != p->device)
+    return fail(RPKV_ERR_INVALID_ARG, "attend on a device other than the plan's");
+  rpkv::AttnArgs a{};
+  a.q = q;
+  a.kpool = kpool;
+  a.vpool = vpool;
+  a.out = out;
+  a.page_table = p->page_table;
+  a.pt_stride = p->pt_stride;
+  a.toklist = (const int32_t *)(p->dmeta + p->off_tok);
+  a.tok_pbase = (const int32_t *)(p->dmeta + p->off_pbase);
+  a.o_part = p->o_part;
+  a.lse_part = p->lse_part;
+  a.Hq = p->s.Hq;
+  a.Hkv = p->s.Hkv;
+  a.G = p->s.G();
+  a.D = p->s.D;
+  a.log2P = p->s.log2P;
+  a.num_pages = p->s.num_pages;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  rpkv::AttnArgs pre = a, dec = a;
+  pre.items = (const Item *)(p->dmeta + p->off_pre);
+  pre.n_items = (int32_t)hp.prefill.size();
+  dec.items = (const Item *)(p->dmeta + p->off_dec);
+  dec.n_items = (int32_t)hp.decode.size();
+  rpkv_status st = RPKV_OK;
+  if (p->s.dtype == RPKV_BF16) {
+    if (pre.n_items > 0)
+      st = timed(p, RPKV_KERNEL_PREFILL, stream, [&] { return rpkv::launch_prefill_bf16(pre, stream); },
+                 "prefill launch");
+    if (st == RPKV_OK && dec.n_items > 0)
+      st = timed(p, RPKV_KERNEL_DECODE, stream, [&] { return rpkv::launch_decode_bf16(dec, stream); },
+                 "decode launch");
+  } else {
+    if (pre.n_items > 0)
+      st = timed(p, RPKV_KERNEL_F32, stream, [&] { return rpkv::launch_attn_f32(pre, stream); },
+                 "fp32 launch");
+    if (st == RPKV_OK && dec.n_items > 0)
+      st = timed(p, RPKV_KERNEL_F32, stream, [&] { return rpkv::launch_attn_f32(dec, stream); },
+                 "fp32 launch");
+  }
+  if (st == RPKV_OK && !hp.merge.empty()) {
+    const int32_t *mg = (const int32_t *)(p->dmeta + p->off_merge);
+    st = timed(p, RPKV_KERNEL_MERGE, stream, [&] {
+      return rpkv::launch_merge(mg, (int32_t)(hp.merge.size() / 3), p->o_part, p->lse_part, out,
+                                p->s.Hq, p->s.D, p->s.dtype, stream);
+    }, "merge launch");
+  }
+  return st;
+}
+
+rpkv_status rpkv_forward(rpkv_plan *p, const void *q, const void *k, const void *v,
+                         const int32_t *slots, void *kpool, void *vpool, void *out, float scale,
+                         void *stream) {
+  if (!p) return fail(RPKV_ERR_INVALID_ARG, "plan is NULL");
+  if (!p->prepared) return fail(RPKV_ERR_NOT_PREPARED, "forward before a successful prepare_metadata");
+  if (p->hp.T > 0 && (!q || !out))
+    return fail(RPKV_ERR_INVALID_ARG, "q and out must be non-NULL");
+  rpkv_status st = rpkv_store_kv(p, k, v, slots, p->hp.T, kpool, vpool, stream);
+  if (st != RPKV_OK) return st;
+  return rpkv_attend(p, q, kpool, vpool, out, scale, stream);
+}
+
+rpkv_status rpkv_timing_enable(rpkv_plan *p, int32_t enable, int32_t max_launches) {
+  if (!p) return fail(RPKV_ERR_INVALID_ARG, "plan is NULL");
+  if (enable && max_launches <= 0) return fail(RPKV_ERR_INVALID_ARG, "max_launches must be > 0");
+  p->timing = enable != 0;
+  if (!enable) return RPKV_OK;
+  while ((int32_t)p->ev.size() < 2 * max_launches) {
+    hipEvent_t e;
+    int err = hipEventCreate(&e);
+    if (err) return hip_fail(err, "hipEventCreate");
+    p->ev.push_back(e);
+  }
+  p->max_launches = max_launches;
+  p->ev_kind.assign(max_launches, 0);
+  p->n_rec = 0;
+  return RPKV_OK;
+}
+
+rpkv_status rpkv_timing_collect(rpkv_plan *p, rpkv_kernel_times *out) {
+  if (!p || !out) return fail(RPKV_ERR_INVALID_ARG, "plan or out is NULL");
+  for (int32_t i = 0; i < p->n_rec; ++i) {
+    int e = hipEventSynchronize(p->ev[2 * i + 1]);
+    if (e) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, p->ev[2 * i], p->ev[2 * i + 1]);
+    if (e) return hip_fail(e, "hipEventElapsedTime");
+    out->launches[p->ev_kind[i]] += 1;
+    out->total_ms[p->ev_kind[i]] += ms;
+  }
+  p->n_rec = 0;
+  return RPKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,406 @@
+// Host planner: turns one batch's metadata into the work partition the kernels
+// consume.  Runs once per batch and serves every layer (mini-sglang "The
+// attention backend and a reference implementation", "The interface"; vLLM
+// "Attention backends", Step 5: one metadata object for all layers of a group).
+//
+// What it decides:
+//  * classification: a request whose n * G query rows fit one 16-column MFMA
+//    tile is decode-type and runs on the split-KV kernel; the others are
+//    prefill-type and run on 128-row MFMA tiles (SGLang walkthrough, section 6:
+//    a mixed batch is split by token between decode and prefill work; "Variable-
+//    length batching and one mixed forward pass", exercise 2: decode work uses
+//    split-KV kernels);
+//  * prefill tiles: 128 / G tokens x G heads of one KV head per tile, key range
+//    cut at the tile's last causal position (bottom-right mask);
+//  * split-KV chunks: one chunk length for the whole batch, chosen ahead of time
+//    so the decode launch has about `split_target` items (vLLM's FlashAttention
+//    metadata carries ahead-of-time scheduler data and a split count);
+//  * cascade: eligible members of a shared-prefix group get prefix tiles that
+//    stack all members' rows against the shared keys, plus their own tail chunks;
+//    the partials are merged by log-sum-exp (SGLang walkthrough 3.3);
+//  * partial-result layout and the merge list;
+//  * launch order: prefill tiles that read the same K/V go to the same XCD
+//    (blocks are dealt round-robin to the 8 XCDs, each with its own L2), and
+//    each XCD's queue runs longest work first.
+#include <algorithm>
+#include <chrono>
+#include <cstring>
+#include <numeric>
+#include <string>
+
+#include "rpkv_internal.h"
+
+namespace rpkv {
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+rpkv_status check_shape(const rpkv_shape *s, Shape *o, std::string *msg) {
+  if (!s) {
+    *msg = "shape is NULL";
+    return RPKV_ERR_INVALID_ARG;
+  }
+  if (s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->num_q_heads % s->num_kv_heads) {
+    *msg = "num_q_heads and num_kv_heads must be positive and Hq % Hkv == 0";
+    return RPKV_ERR_INVALID_ARG;
+  }
+  if (s->num_q_heads / s->num_kv_heads > kPrefillRows) {
+    *msg = "Hq / Hkv above 128 is not supported";
+    return RPKV_ERR_UNSUPPORTED;
+  }
+  if (s->dtype != RPKV_BF16 && s->dtype != RPKV_F32) {
+    *msg = "dtype must be RPKV_BF16 or RPKV_F32";
+    return RPKV_ERR_INVALID_ARG;
+  }
+  if (s->head_dim <= 0) {
+    *msg = "head_dim must be positive";
+    return RPKV_ERR_INVALID_ARG;
+  }
+  if (s->dtype == RPKV_BF16 && s->head_dim != 128) {
+    *msg = "bf16 kernels are built for head_dim 128";
+    return RPKV_ERR_UNSUPPORTED;
+  }
+  if (s->dtype == RPKV_F32 && s->head_dim != 64 && s->head_dim != 128) {
+    *msg = "fp32 kernels are built for head_dim 64 and 128";
+    return RPKV_ERR_UNSUPPORTED;
+  }
+  if (s->page_size < 1 || s->page_size > 1024 || (s->page_size & (s->page_size - 1))) {
+    *msg = "page_size must be a power of two in [1, 1024]";
+    return RPKV_ERR_UNSUPPORTED;
+  }
+  if (s->max_batch <= 0 || s->num_pages <= 0 || s->max_tokens <= 0 ||
+      s->max_pages_per_req <= 0) {
+    *msg = "max_batch, num_pages, max_tokens and max_pages_per_req must be positive";
+    return RPKV_ERR_INVALID_ARG;
+  }
+  if (s->num_pages * (int64_t)s->page_size > INT32_MAX || s->max_tokens > INT32_MAX ||
+      (int64_t)s->max_pages_per_req * s->page_size > INT32_MAX) {
+    *msg = "slots, tokens and sequence lengths must fit int32";
+    return RPKV_ERR_INVALID_ARG;
+  }
+  if (s->decode_max_rows < 0 || s->decode_max_rows > kDecodeRows || s->split_target < 0 ||
+      s->split_min_keys < 0) {
+    *msg = "tuning fields out of range (decode_max_rows <= 16, others >= 0)";
+    return RPKV_ERR_INVALID_ARG;
+  }
+  o->Hq = s->num_q_heads;
+  o->Hkv = s->num_kv_heads;
+  o->D = s->head_dim;
+  o->P = s->page_size;
+  o->log2P = 0;
+  while ((1 << o->log2P) < s->page_size) ++o->log2P;
+  o->dtype = s->dtype;
+  o->max_batch = s->max_batch;
+  o->max_pages_per_req = s->max_pages_per_req;
+  o->num_pages = s->num_pages;
+  o->max_tokens = s->max_tokens;
+  o->decode_max_rows = s->decode_max_rows ? s->decode_max_rows : kDecodeRows;
+  o->split_target = s->split_target ? s->split_target : 8192;
+  o->split_min_keys = (int32_t)round_up(s->split_min_keys ? s->split_min_keys : 256, kDecodeKeys);
+  return RPKV_OK;
+}
+
+namespace {
+
+int64_t item_work(const Item &it) {
+  // key tiles touched; every tile costs the same MFMA work for a full tile
+  return it.ntok ? cdiv(std::max(it.kend - it.kbeg, 1), kPrefillKeys) : 0;
+}
+
+// Deal prefill items to per-XCD queues: items sharing K/V (same group key)
+// stay on one XCD, groups larger than a fair share are cut into contiguous
+// pieces, pieces are placed longest-first on the least loaded queue, each queue
+// runs longest-first, and the queues are interleaved so block b runs on XCD b%8.
+std::vector<Item> xcd_order(const std::vector<Item> &items, const std::vector<int64_t> &gkey) {
+  std::vector<Item> out;
+  if (items.empty()) return out;
+  std::vector<size_t> idx(items.size());
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return gkey[a] < gkey[b]; });
+  int64_t total = 0;
+  for (auto &it : items) total += item_work(it);
+  const int64_t share = std::max<int64_t>(1, cdiv(total, kNumXcd));
+  struct Piece {
+    std::vector<size_t> members;
+    int64_t work = 0;
+  };
+  std::vector<Piece> pieces;
+  size_t i = 0;
+  while (i < idx.size()) {
+    size_t j = i;
+    int64_t gw = 0;
+    while (j < idx.size() && gkey[idx[j]] == gkey[idx[i]]) gw += item_work(items[idx[j++]]);
+    const int64_t npieces = std::max<int64_t>(1, cdiv(gw, share));
+    const int64_t per = cdiv(gw, npieces);
+    Piece cur;
+    for (size_t k = i; k < j; ++k) {
+      cur.members.push_back(idx[k]);
+      cur.work += item_work(items[idx[k]]);
+      if (cur.work >= per && (int64_t)pieces.size() < INT32_MAX) {
+        pieces.push_back(std::move(cur));
+        cur = Piece();
+      }
+    }
+    if (!cur.members.empty()) pieces.push_back(std::move(cur));
+    i = j;
+  }
+  std::stable_sort(pieces.begin(), pieces.end(),
+                   [](const Piece &a, const Piece &b) { return a.work > b.work; });
+  std::vector<std::vector<size_t>> q(kNumXcd);
+  std::vector<int64_t> load(kNumXcd, 0);
+  for (auto &p : pieces) {
+    int best = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    load[best] += p.work;
+    q[best].insert(q[best].end(), p.members.begin(), p.members.end());
+  }
+  size_t qlen = 0;
+  for (auto &qq : q) {
+    std::stable_sort(qq.begin(), qq.end(),
+                     [&](size_t a, size_t b) { return item_work(items[a]) > item_work(items[b]); });
+    qlen = std::max(qlen, qq.size());
+  }
+  Item pad{};
+  pad.ntok = 0;
+  out.assign(qlen * kNumXcd, pad);
+  for (int x = 0; x < kNumXcd; ++x)
+    for (size_t k = 0; k < q[x].size(); ++k) out[k * kNumXcd + x] = items[q[x][k]];
+  return out;
+}
+
+}  // namespace
+
+rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, const int32_t *L,
+                            int32_t cols, const int32_t *pt_host, const rpkv_prefix_group *groups,
+                            int32_t ngroups, HostPlan *out, std::string *msg) {
+  auto t_start = std::chrono::steady_clock::now();
+  HostPlan p;
+  // ------------------------------------------------------------ validation
+  if (batch < 0) {
+    *msg = "batch must be >= 0";
+    return RPKV_ERR_INVALID_ARG;
+  }
+  if (batch > s.max_batch) {
+    *msg = "batch exceeds the plan's max_batch";
+    return RPKV_ERR_CAPACITY;
+  }
+  if (!cu) {
+    *msg = "cu_seqlens_q_host is NULL";
+    return RPKV_ERR_INVALID_ARG;
+  }
+  if (batch > 0 && !L) {
+    *msg = "cache_seqlens_host is NULL";
+    return RPKV_ERR_INVALID_ARG;
+  }
+  if (cu[0] != 0) {
+    *msg = "cu_seqlens_q[0] must be 0";
+    return RPKV_ERR_INVALID_ARG;
+  }
+  if (cols < 0 || ngroups < 0 || (ngroups > 0 && !groups)) {
+    *msg = "page_table_cols and num_groups must be >= 0 (groups non-NULL when num_groups > 0)";
+    return RPKV_ERR_INVALID_ARG;
+  }
+  if (cols > s.max_pages_per_req) {
+    *msg = "page_table_cols exceeds the plan's max_pages_per_req";
+    return RPKV_ERR_CAPACITY;
+  }
+  for (int32_t i = 0; i < batch; ++i) {
+    const int64_t n = (int64_t)cu[i + 1] - cu[i];
+    if (n < 0) {
+      *msg = "cu_seqlens_q must be non-decreasing (request " + std::to_string(i) + ")";
+      return RPKV_ERR_INVALID_ARG;
+    }
+    if (L[i] < 0 || n > L[i]) {
+      *msg = "request " + std::to_string(i) + " has more queries than KV (n > L) or L < 0";
+      return RPKV_ERR_INVALID_ARG;
+    }
+    if (cdiv(L[i], s.P) > cols) {
+      *msg = "request " + std::to_string(i) + " needs more page-table columns than given";
+      return RPKV_ERR_INVALID_ARG;
+    }
+  }
+  const int64_t T64 = batch ? cu[batch] : 0;
+  if (T64 > s.max_tokens) {
+    *msg = "number of tokens exceeds the plan's max_tokens";
+    return RPKV_ERR_CAPACITY;
+  }
+  if (pt_host) {
+    for (int32_t i = 0; i < batch; ++i)
+      for (int64_t c = 0; c < cdiv(L[i], s.P); ++c) {
+        const int32_t id = pt_host[(int64_t)i * cols + c];
+        if (id < 0 || id >= s.num_pages) {
+          *msg = "page id out of [0, num_pages) in row " + std::to_string(i);
+          return RPKV_ERR_INVALID_ARG;
+        }
+      }
+  }
+  std::vector<int32_t> in_group(batch, -1);
+  for (int32_t g = 0; g < ngroups; ++g) {
+    const rpkv_prefix_group &gr = groups[g];
+    if (gr.first_req < 0 || gr.num_reqs < 0 || (int64_t)gr.first_req + gr.num_reqs > batch ||
+        gr.prefix_len < 0 || gr.prefix_len % s.P) {
+      *msg = "cascade group " + std::to_string(g) +
+             " out of range or prefix_len not a multiple of page_size";
+      return RPKV_ERR_INVALID_ARG;
+    }
+    for (int32_t j = gr.first_req; j < gr.first_req + gr.num_reqs; ++j) {
+      if (in_group[j] >= 0) {
+        *msg = "cascade groups overlap at request " + std::to_string(j);
+        return RPKV_ERR_INVALID_ARG;
+      }
+      in_group[j] = g;
+      if (pt_host && L[j] >= gr.prefix_len) {
+        for (int64_t c = 0; c < gr.prefix_len / s.P; ++c)
+          if (pt_host[(int64_t)j * cols + c] != pt_host[(int64_t)gr.first_req * cols + c]) {
+            *msg = "cascade group " + std::to_string(g) + ": request " + std::to_string(j) +
+                   " does not share the prefix pages";
+            return RPKV_ERR_INVALID_ARG;
+          }
+      }
+    }
+  }
+
+  // ------------------------------------------------------------ metadata
+  const int32_t T = (int32_t)T64;
+  const int32_t G = s.G();
+  p.batch = batch;
+  p.T = T;
+  p.cu_q.assign(cu, cu + batch + 1);
+  p.L.assign(L, L + batch);
+  for (int32_t i = 0; i < batch; ++i) {
+    p.max_q = std::max(p.max_q, cu[i + 1] - cu[i]);
+    p.max_k = std::max(p.max_k, L[i]);
+  }
+  const bool f32 = s.dtype == RPKV_F32;
+  const int32_t tile_rows = f32 ? kF32Rows : kPrefillRows;
+  const int32_t tpt = std::max(1, tile_rows / G);  // tokens per prefill tile
+  auto n_of = [&](int32_t i) { return cu[i + 1] - cu[i]; };
+  auto is_decode = [&](int32_t i) {
+    return n_of(i) > 0 && (int64_t)n_of(i) * G <= s.decode_max_rows;
+  };
+
+  // cascade eligibility: decode-type members whose new tokens lie past the prefix
+  std::vector<std::vector<int32_t>> casc(ngroups);
+  std::vector<char> is_member(batch, 0);
+  for (int32_t g = 0; g < ngroups; ++g) {
+    const rpkv_prefix_group &gr = groups[g];
+    if (gr.prefix_len <= 0) continue;
+    std::vector<int32_t> m;
+    for (int32_t j = gr.first_req; j < gr.first_req + gr.num_reqs; ++j)
+      if (is_decode(j) && L[j] - n_of(j) >= gr.prefix_len) m.push_back(j);
+    if (m.size() >= 2) {
+      for (int32_t j : m) is_member[j] = 1;
+      casc[g] = std::move(m);
+    }
+  }
+
+  // split-KV chunk: one length for the batch, sized for ~split_target items
+  int64_t dec_keys = 0;
+  for (int32_t i = 0; i < batch; ++i) {
+    if (!is_decode(i)) continue;
+    dec_keys += (int64_t)(is_member[i] ? L[i] - groups[in_group[i]].prefix_len : L[i]) * s.Hkv;
+  }
+  const int64_t chunk64 =
+      std::max<int64_t>(s.split_min_keys, round_up(cdiv(dec_keys, s.split_target), kDecodeKeys));
+  const int32_t chunk = (int32_t)std::min<int64_t>(chunk64, 1 << 30);
+  p.decode_chunk = chunk;
+
+  std::vector<int32_t> nsplit(T, 1);
+  std::vector<Item> pre, dec;
+  std::vector<int64_t> pre_key;  // K/V-sharing group key per prefill item
+
+  // decode-type requests outside any cascade
+  for (int32_t i = 0; i < batch; ++i) {
+    if (!is_decode(i) || is_member[i]) continue;
+    const int32_t n = n_of(i);
+    const int32_t ns = (int32_t)cdiv(L[i], chunk);
+    for (int32_t t = cu[i]; t < cu[i + 1]; ++t) nsplit[t] = ns;
+    for (int32_t h = 0; h < s.Hkv; ++h)
+      for (int32_t c = 0; c < ns; ++c)
+        dec.push_back(Item{i, h, cu[i], n, L[i] - n, c * chunk, std::min(L[i], (c + 1) * chunk),
+                           ns > 1 ? c : -1});
+  }
+
+  // prefill-type requests
+  for (int32_t i = 0; i < batch; ++i) {
+    const int32_t n = n_of(i);
+    if (n == 0 || is_decode(i)) continue;
+    for (int32_t h = 0; h < s.Hkv; ++h)
+      for (int32_t r0 = 0; r0 < n; r0 += tpt) {
+        const int32_t r1 = std::min(n, r0 + tpt);
+        pre.push_back(Item{i, h, cu[i] + r0, r1 - r0, L[i] - n + r0, 0, L[i] - n + r1, -1});
+        pre_key.push_back((int64_t)i * s.Hkv + h);
+      }
+  }
+
+  // cascade groups
+  for (int32_t g = 0; g < ngroups; ++g) {
+    if (casc[g].empty()) continue;
+    const int32_t prefix = groups[g].prefix_len;
+    const int32_t off = (int32_t)p.toklist.size();
+    for (int32_t j : casc[g])
+      for (int32_t t = cu[j]; t < cu[j + 1]; ++t) p.toklist.push_back(t);
+    const int32_t nt = (int32_t)p.toklist.size() - off;
+    const int32_t ntile = (int32_t)cdiv(nt, tpt);
+    // prefix chunks: enough tiles to spread over the chip, chunks >= 256 keys
+    int64_t npc = cdiv(512, (int64_t)ntile * s.Hkv);
+    npc = std::max<int64_t>(1, std::min<int64_t>(npc, prefix / 256));
+    const int32_t pchunk = (int32_t)round_up(cdiv(prefix, npc), kPrefillKeys);
+    npc = cdiv(prefix, pchunk);
+    for (int32_t h = 0; h < s.Hkv; ++h)
+      for (int32_t tl = 0; tl < ntile; ++tl)
+        for (int32_t c = 0; c < npc; ++c) {
+          const int32_t a = tl * tpt, b = std::min(nt, a + tpt);
+          pre.push_back(Item{casc[g][0], h, off + a, b - a, -1, c * pchunk,
+                             std::min(prefix, (c + 1) * pchunk), c});
+          pre_key.push_back(((int64_t)batch + g) * s.Hkv + h);
+          ++p.n_cascade_items;
+        }
+    for (int32_t j : casc[g]) {
+      const int32_t n = n_of(j);
+      const int32_t ns = (int32_t)cdiv(L[j] - prefix, chunk);
+      for (int32_t t = cu[j]; t < cu[j + 1]; ++t) nsplit[t] = (int32_t)npc + ns;
+      for (int32_t h = 0; h < s.Hkv; ++h)
+        for (int32_t c = 0; c < ns; ++c)
+          dec.push_back(Item{j, h, cu[j], n, L[j] - n, prefix + c * chunk,
+                             std::min(L[j], prefix + (c + 1) * chunk), (int32_t)npc + c});
+      ++p.cascade_members;
+    }
+  }
+
+  // partials and merge list
+  p.tok_pbase.assign(T, -1);
+  int64_t np = 0;
+  for (int32_t t = 0; t < T; ++t)
+    if (nsplit[t] >= 2) {
+      p.tok_pbase[t] = (int32_t)np;
+      p.merge.push_back(t);
+      p.merge.push_back((int32_t)np);
+      p.merge.push_back(nsplit[t]);
+      np += nsplit[t];
+    }
+  if (np > INT32_MAX) {
+    *msg = "too many partial results";
+    return RPKV_ERR_CAPACITY;
+  }
+  p.n_partials = np;
+
+  // launch order
+  p.n_prefill_real = (int32_t)pre.size();
+  if (f32) {
+    std::stable_sort(pre.begin(), pre.end(),
+                     [](const Item &a, const Item &b) { return item_work(a) > item_work(b); });
+    p.prefill = std::move(pre);
+  } else {
+    p.prefill = xcd_order(pre, pre_key);
+  }
+  std::stable_sort(dec.begin(), dec.end(), [](const Item &a, const Item &b) {
+    return (a.kend - a.kbeg) > (b.kend - b.kbeg);
+  });
+  p.decode = std::move(dec);
+  p.plan_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_start)
+                  .count();
+  *out = std::move(p);
+  return RPKV_OK;
+}
+
+}  // namespace rpkv

@@ -1,0 +1,100 @@
+// Internal declarations shared by the planner, the launcher and the kernels.
+// Not part of the ABI (the ABI is include/rpkv.h).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "rpkv.h"
+
+namespace rpkv {
+
+// One unit of attention work.  For the MFMA prefill kernel an item is one
+// workgroup (a tile of up to kPrefillRows query rows x one KV head); for the
+// split-KV decode kernel an item is one wavefront (up to 16 rows); for the fp32
+// kernel one workgroup of up to kF32Rows rows.  Rows are (token, head-in-group)
+// pairs, token-major: row m -> token tok0 + m / G, query head kvh*G + m % G.
+struct Item {
+  int32_t req;   // request index: its page-table row is read
+  int32_t kvh;   // KV head
+  int32_t tok0;  // first packed token, or offset into the cascade token list
+  int32_t ntok;  // tokens in the tile; 0 = padding item (skipped)
+  int32_t pos0;  // absolute position of tok0's query; -1 marks a cascade prefix
+                 // tile (tokens from the list, every key in range visible)
+  int32_t kbeg;  // keys [kbeg, kend) of the request are attended
+  int32_t kend;
+  int32_t split; // -1: write the final output; >= 0: write partial number
+                 // `split` of each token (partial index tok_pbase[t] + split)
+};
+static_assert(sizeof(Item) == 32, "Item is 8 int32");
+
+constexpr int kPrefillRows = 128;     // bf16 MFMA tile: 4 waves x 32 rows
+constexpr int kPrefillKeys = 64;      // keys per LDS tile
+constexpr int kDecodeRows = 16;       // bf16 split-KV item: 16 MFMA columns
+constexpr int kDecodeKeys = 32;       // keys per decode step
+constexpr int kDecodeWavesPerBlock = 4;
+constexpr int kF32Rows = 16;          // fp32 tile rows
+constexpr int kF32Keys = 32;          // fp32 keys per LDS tile
+constexpr int kNumXcd = 8;            // MI355X: 8 XCDs, blocks go round-robin
+
+struct HostPlan {
+  int32_t batch = 0, T = 0, max_q = 0, max_k = 0;
+  std::vector<int32_t> cu_q, L;
+  std::vector<Item> prefill;   // XCD-interleaved, padded to a multiple of 8
+  std::vector<Item> decode;    // longest first
+  std::vector<int32_t> tok_pbase;  // [T] partial base or -1
+  std::vector<int32_t> merge;      // [M][3] token, partial base, count
+  std::vector<int32_t> toklist;    // cascade token lists
+  int64_t n_partials = 0;
+  int32_t n_cascade_items = 0, cascade_members = 0, decode_chunk = 0;
+  int32_t n_prefill_real = 0;      // items before padding
+  double plan_us = 0;
+};
+
+struct Shape {
+  int32_t Hq, Hkv, D, P, log2P, dtype, max_batch, max_pages_per_req;
+  int64_t num_pages, max_tokens;
+  int32_t decode_max_rows, split_target, split_min_keys;
+  int32_t G() const { return Hq / Hkv; }
+};
+
+// Validate a shape; on failure returns the status and fills msg.
+rpkv_status check_shape(const rpkv_shape *s, Shape *out, std::string *msg);
+
+// Build the work partition of one batch on the host.
+rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu,
+                            const int32_t *L, int32_t cols, const int32_t *pt_host,
+                            const rpkv_prefix_group *groups, int32_t ngroups, HostPlan *out,
+                            std::string *msg);
+
+// Kernel launchers (defined in the .hip files).  All enqueue on `stream`.
+struct AttnArgs {
+  const void *q;
+  const void *kpool;
+  const void *vpool;
+  void *out;
+  const int32_t *page_table;
+  int64_t pt_stride;
+  const Item *items;
+  int32_t n_items;
+  const int32_t *toklist;
+  const int32_t *tok_pbase;
+  float *o_part;      // [partials, Hq, D]
+  float *lse_part;    // [partials, Hq] (base-2 log-sum-exp of scaled logits)
+  int32_t Hq, Hkv, G, D, log2P;
+  int64_t num_pages;
+  float scale_log2;   // scale * log2(e)
+};
+
+int launch_store_kv(const void *k, const void *v, const int32_t *slots, int64_t T,
+                    int64_t row_bytes, int64_t num_slots, void *kpool, void *vpool,
+                    void *stream);
+int launch_prefill_bf16(const AttnArgs &a, void *stream);
+int launch_decode_bf16(const AttnArgs &a, void *stream);
+int launch_attn_f32(const AttnArgs &a, void *stream);
+int launch_merge(const int32_t *merge, int32_t n_merge, const float *o_part,
+                 const float *lse_part, void *out, int32_t Hq, int32_t D, int32_t dtype,
+                 void *stream);
+
+}  // namespace rpkv

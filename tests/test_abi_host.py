@@ -1,0 +1,233 @@
+"""Host-side tests of the C ABI (no GPU): the library loads and exports every
+function the header declares, capability checks, validation errors, and the
+planner's work partition covers every visible (token, head, key) exactly once."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from tests import _golden
+from workloads import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def rp():
+    import ragged_paged_kv_store_amd as rp
+    return rp
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "rpkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rpkv_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(rp):
+    declared = header_functions()
+    assert len(declared) >= 15
+    lib = ctypes.CDLL(rp.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(rp.EXPORTS) == declared
+
+
+def test_status_strings(rp):
+    for code, name in rp.STATUS.items():
+        assert rp.lib.rpkv_status_string(code).decode() == name
+
+
+BASE = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, dtype=0, max_batch=64,
+            num_pages=1024, max_tokens=8192, max_pages_per_req=512)
+
+
+@pytest.mark.parametrize("change,ok", [
+    ({}, True),
+    (dict(head_dim=64), False),             # bf16 kernels are built for 128
+    (dict(dtype=1, head_dim=64), True),
+    (dict(dtype=1, head_dim=96), False),
+    (dict(num_q_heads=30), False),          # Hq % Hkv
+    (dict(page_size=12), False),            # not a power of two
+    (dict(page_size=1), True),
+    (dict(num_kv_heads=32), True),          # MHA
+    (dict(num_kv_heads=1), True),           # G = 32
+    (dict(dtype=7), False),
+    (dict(decode_max_rows=17), False),
+])
+def test_supports(rp, change, ok):
+    got, msg = rp.supports(**{**BASE, **change})
+    assert got == ok, msg
+
+
+def make_plan(rp, spec, **kw):
+    return rp.Plan(num_q_heads=spec.Hq, num_kv_heads=spec.Hkv, head_dim=spec.D,
+                   page_size=spec.P, dtype=0 if spec.dtype == "bf16" else 1,
+                   max_batch=max(spec.bs, 1), num_pages=spec.num_pages,
+                   max_tokens=max(spec.T, 1), max_pages_per_req=spec.page_table.shape[1], **kw)
+
+
+def test_last_indices_worked_example(rp):
+    g = _golden.load("p1_worked_example.txt")
+    p = rp.Plan(num_q_heads=16, num_kv_heads=8, head_dim=128, page_size=1, dtype=0, max_batch=3,
+                num_pages=64, max_tokens=16, max_pages_per_req=9)
+    p.plan_host(g["cu_seqlens_q"], g["cache_seqlens"], 9, np.array(g["page_table_cut"]))
+    assert p.last_indices().tolist() == g["last_indices"]
+    # a request with no queries gets -1
+    p.plan_host([0, 2, 2, 3], [4, 5, 6], 9)
+    assert p.last_indices().tolist() == [1, -1, 2]
+
+
+@pytest.mark.parametrize("cu,L,cols,pt,status", [
+    ([1, 2], [2], 2, None, 1),          # cu[0] != 0
+    ([0, 3, 2], [3, 3], 2, None, 1),    # decreasing
+    ([0, 4], [3], 2, None, 1),          # n > L
+    ([0, 1], [40], 2, None, 1),         # needs 3 columns of 16
+    ([0, 1], [4], 2, [[5000, 0]], 1),   # page id out of range (host table given)
+    ([0, 1], [4], 2, [[-1, 0]], 1),     # negative page id
+])
+def test_invalid_batches_rejected(rp, cu, L, cols, pt, status):
+    p = rp.Plan(**BASE)
+    with pytest.raises(rp.RpkvError) as e:
+        p.plan_host(cu, L, cols, None if pt is None else np.array(pt))
+    assert e.value.status == status
+
+
+def test_capacity_errors(rp):
+    p = rp.Plan(**{**BASE, "max_batch": 2, "max_tokens": 4})
+    with pytest.raises(rp.RpkvError) as e:
+        p.plan_host([0, 1, 2, 3], [1, 1, 1], 1)
+    assert e.value.status == 6
+    with pytest.raises(rp.RpkvError) as e:
+        p.plan_host([0, 5], [5], 1)
+    assert e.value.status == 6
+
+
+def test_not_prepared_errors(rp):
+    p = rp.Plan(**BASE)
+    with pytest.raises(rp.RpkvError) as e:
+        p.info()
+    assert e.value.status == 4
+    st = rp.lib.rpkv_attend(p._h, None, None, None, None, 0.1, None)
+    assert st == 4
+
+
+def test_cascade_hint_checked_against_host_table(rp):
+    p = rp.Plan(**BASE)
+    pt = np.array([[1, 2, 3], [1, 2, 4], [1, 9, 5]], np.int32)
+    p.plan_host([0, 1, 2, 3], [40, 40, 40], 3, pt, groups=[(0, 2, 32)])
+    with pytest.raises(rp.RpkvError):
+        p.plan_host([0, 1, 2, 3], [40, 40, 40], 3, pt, groups=[(0, 3, 32)])
+    with pytest.raises(rp.RpkvError):   # not a multiple of the page size
+        p.plan_host([0, 1, 2, 3], [40, 40, 40], 3, pt, groups=[(0, 2, 20)])
+    with pytest.raises(rp.RpkvError):   # overlapping groups
+        p.plan_host([0, 1, 2, 3], [40, 40, 40], 3, pt, groups=[(0, 2, 16), (1, 2, 16)])
+
+
+# ------------------------------------------------------------------ coverage
+
+def check_coverage(rp, plan, spec):
+    """Every visible (token, q head, key) is covered by exactly one item, split
+    numbers of a (token, head) are -1 alone or exactly 0..S-1, cascade tiles only
+    cover keys every row can see, and key ranges never pass L."""
+    G = spec.G
+    cu = spec.cu_q
+    tok_req = np.repeat(np.arange(spec.bs), spec.n)
+    tl = plan.token_list()
+    cover = {}
+    for kind in (0, 1):
+        for it in plan.items(kind):
+            req, kvh, tok0, ntok, pos0, kbeg, kend, split = [int(x) for x in it]
+            if ntok == 0:
+                continue
+            assert 0 <= kbeg < kend
+            if kind == 1:
+                assert ntok * G <= 16
+            else:
+                assert ntok * G <= (128 if spec.dtype == "bf16" else 16) or ntok == 1
+            for r in range(ntok):
+                if pos0 < 0:
+                    t = int(tl[tok0 + r])
+                else:
+                    t = tok0 + r
+                i = int(tok_req[t])
+                a = int(spec.L[i]) - int(spec.n[i]) + (t - int(cu[i]))
+                if pos0 >= 0:
+                    assert i == req and pos0 + r == a
+                    hi = min(kend, a + 1)
+                else:
+                    assert kend - 1 <= a, "cascade tile covers a key a row cannot see"
+                    hi = kend
+                assert kend <= int(spec.L[i]) or pos0 < 0
+                for g in range(G):
+                    h = kvh * G + g
+                    cover.setdefault((t, h), []).append((kbeg, hi, split))
+    for t in range(spec.T):
+        i = int(tok_req[t])
+        a = int(spec.L[i]) - int(spec.n[i]) + (t - int(cu[i]))
+        for h in range(spec.Hq):
+            segs = sorted(cover.get((t, h), []))
+            assert segs, (t, h)
+            pos = 0
+            for lo, hi, _ in segs:
+                if hi <= lo:
+                    continue
+                assert lo == pos, (t, h, segs)
+                pos = hi
+            assert pos == a + 1, (t, h, segs)
+            splits = sorted(s for _, _, s in segs)
+            assert splits == [-1] or splits == list(range(len(segs))), (t, h, splits)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_small_configs_covered_exactly_once(rp, cid):
+    spec = synth.small_config(cid)
+    p = make_plan(rp, spec)
+    p.plan_host(spec.cu_q, spec.L, spec.page_table.shape[1], spec.page_table, spec.groups)
+    check_coverage(rp, p, spec)
+    if spec.groups:
+        assert p.info()["cascade_members"] == spec.groups[0][1]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_batches_covered_exactly_once(rp, seed):
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([1, 2, 4, 7, 8, 16]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    P = int(rng.choice([1, 4, 16, 64]))
+    bs = int(rng.integers(1, 12))
+    n, L = [], []
+    for _ in range(bs):
+        kind = rng.integers(0, 4)
+        if kind == 0:
+            x = int(rng.integers(1, 300)); n.append(x); L.append(x)
+        elif kind == 1:
+            L.append(int(rng.integers(1, 3000))); n.append(1)
+        elif kind == 2:
+            l = int(rng.integers(2, 2000)); L.append(l); n.append(int(rng.integers(1, min(l, 3) + 1)))
+        else:
+            L.append(int(rng.integers(0, 50))); n.append(0)
+    dtype = "bf16" if seed % 3 else "f32"
+    spec = synth.build("r", dtype, G * Hkv, Hkv, 128, P, n, L, seed, np.random.default_rng(seed), 1.2)
+    kw = dict(split_min_keys=int(rng.choice([0, 32, 64])), split_target=int(rng.choice([0, 64])))
+    p = make_plan(rp, spec, **kw)
+    p.plan_host(spec.cu_q, spec.L, spec.page_table.shape[1], spec.page_table)
+    check_coverage(rp, p, spec)
+
+
+def test_full_config_plans(rp):
+    """The five full-size batches plan; their partitions are exactly-once (C2,
+    C4 checked fully; C3/C5 by counts) and the planner is fast."""
+    for cid in (2, 4):
+        spec = synth.full_config(cid)
+        p = make_plan(rp, spec)
+        p.plan_host(spec.cu_q, spec.L, spec.page_table.shape[1], spec.page_table, spec.groups)
+        check_coverage(rp, p, spec)
+    spec = synth.full_config(5)
+    p = make_plan(rp, spec)
+    p.plan_host(spec.cu_q, spec.L, spec.page_table.shape[1], spec.page_table, spec.groups)
+    info = p.info()
+    assert info["cascade_members"] == 64 and info["num_cascade_items"] > 0
+    assert info["plan_host_us"] < 50_000
