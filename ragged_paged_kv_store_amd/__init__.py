@@ -156,6 +156,46 @@ class Plan:
         self.workspace = None      # torch uint8 device tensor, grown on demand
         self._pt = None            # keep the page table alive while prepared
         self.batch = 0
+        self.num_tokens = 0
+
+    # The C ABI takes plain pointers; these checks keep tensors of another shape,
+    # dtype or device from ever reaching a kernel.
+    def _dtype(self):
+        import torch
+        return torch.bfloat16 if self.shape.dtype == BF16 else torch.float32
+
+    def _check_rows(self, name, t, heads, min_rows):
+        if t is None:
+            if min_rows > 0:
+                raise ValueError(f"{name} is required")
+            return
+        sh = self.shape
+        if not t.is_cuda or t.dtype != self._dtype() or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {self._dtype()} CUDA tensor")
+        if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != sh.head_dim:
+            raise ValueError(f"{name} must be [tokens, {heads}, {sh.head_dim}], got {tuple(t.shape)}")
+        if t.shape[0] < min_rows:
+            raise ValueError(f"{name} has {t.shape[0]} rows, the batch has {min_rows} tokens")
+
+    def _check_pool(self, name, t):
+        sh = self.shape
+        want = sh.num_pages * sh.page_size * sh.num_kv_heads * sh.head_dim
+        if t is None or not t.is_cuda or t.dtype != self._dtype() or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {self._dtype()} CUDA tensor")
+        if t.numel() != want or t.shape[-1] != sh.head_dim or t.shape[-2] != sh.num_kv_heads:
+            raise ValueError(f"{name} must hold [num_pages*page_size, Hkv, D] = "
+                             f"[{sh.num_pages * sh.page_size}, {sh.num_kv_heads}, {sh.head_dim}]")
+
+    def _check_slots(self, t, min_rows):
+        import torch
+        if t is None:
+            if min_rows > 0:
+                raise ValueError("slot_mapping is required")
+            return
+        if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous() or t.dim() != 1:
+            raise ValueError("slot_mapping must be a contiguous int32 CUDA vector")
+        if t.numel() < min_rows:
+            raise ValueError("slot_mapping is shorter than the batch")
 
     def close(self):
         if getattr(self, "_h", None):
@@ -196,8 +236,11 @@ class Plan:
         cu = _i32(cu_q)
         sl = _i32(cache_seqlens)
         bs = len(sl)
-        assert page_table.dtype == torch.int32 and page_table.dim() == 2
-        assert page_table.stride(1) == 1
+        if not (page_table.is_cuda and page_table.dtype == torch.int32 and
+                page_table.dim() == 2 and page_table.stride(1) == 1):
+            raise ValueError("page_table must be a 2-D int32 CUDA tensor with unit column stride")
+        if page_table.shape[0] < len(cache_seqlens):
+            raise ValueError("page_table has fewer rows than the batch")
         cols = page_table.shape[1]
         pth = None if page_table_host is None else _i32(page_table_host)
         garr = (PrefixGroup * max(len(groups), 1))(*[PrefixGroup(*g) for g in groups])
@@ -220,6 +263,7 @@ class Plan:
             break
         self._pt = page_table
         self.batch = bs
+        self.num_tokens = int(cu[-1]) if len(cu) else 0
 
     def info(self) -> dict:
         inf = PlanInfo()
@@ -252,15 +296,36 @@ class Plan:
 
     # ------------------------------------------------------------ per layer
     def store_kv(self, k, v, slot_mapping, k_pool, v_pool, stream=None):
+        n = int(slot_mapping.numel()) if slot_mapping is not None else 0
+        self._check_slots(slot_mapping, n)
+        self._check_rows("k", k, self.shape.num_kv_heads, n)
+        self._check_rows("v", v, self.shape.num_kv_heads, n)
+        self._check_pool("k_pool", k_pool)
+        self._check_pool("v_pool", v_pool)
         _check(lib.rpkv_store_kv(self._h, _ptr(k), _ptr(v), _ptr(slot_mapping),
                                  int(slot_mapping.numel()) if slot_mapping is not None else 0,
                                  _ptr(k_pool), _ptr(v_pool), _stream(stream)))
 
     def attend(self, q, k_pool, v_pool, out, scale: float, stream=None):
+        T = self.num_tokens
+        if T > 0:
+            self._check_rows("q", q, self.shape.num_q_heads, T)
+            self._check_rows("out", out, self.shape.num_q_heads, T)
+            self._check_pool("k_pool", k_pool)
+            self._check_pool("v_pool", v_pool)
         _check(lib.rpkv_attend(self._h, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out),
                                float(scale), _stream(stream)))
 
     def forward(self, q, k, v, slot_mapping, k_pool, v_pool, out, scale: float, stream=None):
+        T = self.num_tokens
+        if T > 0:
+            self._check_slots(slot_mapping, T)
+            self._check_rows("q", q, self.shape.num_q_heads, T)
+            self._check_rows("out", out, self.shape.num_q_heads, T)
+            self._check_rows("k", k, self.shape.num_kv_heads, T)
+            self._check_rows("v", v, self.shape.num_kv_heads, T)
+            self._check_pool("k_pool", k_pool)
+            self._check_pool("v_pool", v_pool)
         _check(lib.rpkv_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(slot_mapping),
                                 _ptr(k_pool), _ptr(v_pool), _ptr(out), float(scale),
                                 _stream(stream)))

@@ -266,32 +266,58 @@ def test_store_kv_bitwise_with_padding_slots():
 
 
 def test_one_prepare_serves_many_layers_and_plans_are_reusable():
-    spec = synth.small_config(4)
-    plan = H.make_plan(spec)
+    """One prepare serves several layers (different pools and q/k/v); one plan
+    then serves batches of different sizes (its device buffers grow and shrink).
+    Every batch has the plan's head shape and pool size."""
+    import dataclasses
+    big = synth.c2_llama8b_mixed(seed=31, scale=0.2)
+    small = synth.c2_llama8b_mixed(seed=32, scale=0.1)
+    pool_pages = max(big.num_pages, small.num_pages)
+    cols = max(big.page_table.shape[1], small.page_table.shape[1])
+
+    def widen(spec):
+        pt = np.zeros((spec.bs, cols), np.int32)
+        pt[:, :spec.page_table.shape[1]] = spec.page_table
+        return dataclasses.replace(spec, num_pages=pool_pages, page_table=pt)
+
+    big, small = widen(big), widen(small)
+    plan = rp.Plan(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, dtype=rp.BF16,
+                   max_batch=8, num_pages=pool_pages, max_tokens=max(big.T, small.T),
+                   max_pages_per_req=cols)
     for layer in range(3):
-        ht = synth.host_tensors(spec, seed=100 + layer)
-        ref, _, _, _ = oracle.store_then_attend(spec, ht, nthreads=8)
-        db = H.dev_batch(spec, ht)
+        ht = synth.host_tensors(small, seed=100 + layer)
+        ref, _, _, _ = oracle.store_then_attend(small, ht, nthreads=8)
+        db = H.dev_batch(small, ht)
         if layer == 0:
-            plan.prepare(spec.cu_q, spec.L, db.page_table, spec.page_table)
+            plan.prepare(small.cu_q, small.L, db.page_table, small.page_table)
         out = torch.empty_like(db.q)
-        plan.forward(db.q, db.k, db.v, db.slot_mapping, db.kpool, db.vpool, out, spec.scale)
+        plan.forward(db.q, db.k, db.v, db.slot_mapping, db.kpool, db.vpool, out, small.scale)
         torch.cuda.synchronize()
         assert H.max_err(out, ref) <= 2e-2
-    # a different, larger batch on the same plan (device buffers grow)
-    spec2 = synth.small_config(5)
-    plan2 = H.make_plan(spec2)
-    ht2 = synth.host_tensors(spec2)
-    ref2, _, _, _ = oracle.store_then_attend(spec2, ht2, nthreads=8)
-    db2 = H.dev_batch(spec2, ht2)
-    out2, _ = H.gpu_forward(spec2, db2, plan=plan2)
-    assert H.max_err(out2, ref2) <= 2e-2
-    spec3 = synth.small_config(2)
-    ht3 = synth.host_tensors(spec3)
-    ref3, _, _, _ = oracle.store_then_attend(spec3, ht3, nthreads=8)
-    db3 = H.dev_batch(spec3, ht3)
-    out3, _ = H.gpu_forward(spec3, db3, plan=plan2)
-    assert H.max_err(out3, ref3) <= 2e-2
+    for spec in (big, small):
+        ht = synth.host_tensors(spec)
+        ref, _, _, _ = oracle.store_then_attend(spec, ht, nthreads=8)
+        db = H.dev_batch(spec, ht)
+        out, _ = H.gpu_forward(spec, db, plan=plan)
+        assert H.max_err(out, ref) <= 2e-2
+
+
+def test_binding_rejects_tensors_of_another_shape():
+    spec = synth.small_config(2)
+    ht = synth.host_tensors(spec)
+    db = H.dev_batch(spec, ht)
+    plan = H.make_plan(spec)
+    plan.prepare(spec.cu_q, spec.L, db.page_table, spec.page_table)
+    out = torch.empty_like(db.q)
+    with pytest.raises(ValueError):
+        plan.forward(db.q[:, :16].contiguous(), db.k, db.v, db.slot_mapping, db.kpool, db.vpool,
+                     out, spec.scale)
+    with pytest.raises(ValueError):
+        plan.forward(db.q, db.k, db.v, db.slot_mapping, db.kpool[:-16].contiguous(), db.vpool,
+                     out, spec.scale)
+    with pytest.raises(ValueError):
+        plan.forward(db.q.float(), db.k, db.v, db.slot_mapping, db.kpool, db.vpool, out,
+                     spec.scale)
 
 
 # ---------------------------------------------------------------- full size
