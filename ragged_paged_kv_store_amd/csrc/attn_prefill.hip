@@ -33,9 +33,10 @@ constexpr int KS = D + 8;         // K LDS row stride (bf16), padded
 constexpr int VS = BN + 8;        // V^T LDS row stride (bf16), padded
 }  // namespace
 
-__global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+__global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(AttnArgs a) {
+  // two K/V buffers: step t computes from buffer t%2 while step t+1 is staged
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VS];
 
   const Item it = a.items[blockIdx.x];
   if (it.ntok == 0) return;
@@ -67,7 +68,11 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(AttnArgs a) {
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float mrun = kNegInf, lrun = 0.f;
+  // Running reference max (scaled, base 2) and this lane's part of the row sum.
+  // The reference moves only when the row max passes it by more than 8, so the
+  // exponentials stay <= 2^8 and the O rescale is skipped on most steps.
+  float mref = kNegInf, lrun = 0.f;
+  const float c = a.scale_log2;
 
   // ---- loader roles
   const int32_t *ptrow = a.page_table + (int64_t)it.req * a.pt_stride;
@@ -76,31 +81,37 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(AttnArgs a) {
   const int vkg = tid & 15, vdch = tid >> 4;   // V: keys 4*vkg..+3, channels 8*vdch..+7
   const char *kpool = (const char *)a.kpool;
   const char *vpool = (const char *)a.vpool;
-  const int kend = it.kend;
+  const int kbeg = it.kbeg, kend = it.kend;
+  const int nsteps = (kend - kbeg + BN - 1) / BN;
   u32x4 kreg[4], vreg[4];
+  int32_t pk, pv[4];  // page ids of the loader's keys for the next gather (-1: none)
 
-  auto row_off = [&](int key) -> int64_t {
-    const int pg = clamp_page(ptrow[key >> a.log2P], a.num_pages);
-    const int64_t slot = ((int64_t)pg << a.log2P) + (key & pmask);
+  auto fetch_ids = [&](int kt) {
+    const int key = kt + kkey;
+    pk = key < kend ? ptrow[key >> a.log2P] : -1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kv = kt + 4 * vkg + j;
+      pv[j] = kv < kend ? ptrow[kv >> a.log2P] : -1;
+    }
+  };
+  auto row_off = [&](int32_t page, int key) -> int64_t {
+    const int64_t slot = ((int64_t)clamp_page(page, a.num_pages) << a.log2P) + (key & pmask);
     return (slot * a.Hkv + it.kvh) * (D * 2);
   };
   auto gather = [&](int kt) {
-    {
-      const int key = kt + kkey;
-      if (key < kend) {
-        const char *src = kpool + row_off(key) + kpart * 64;
+    if (pk >= 0) {
+      const char *src = kpool + row_off(pk, kt + kkey) + kpart * 64;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kreg[j] = *(const u32x4 *)(src + 16 * j);
-      } else {
+      for (int j = 0; j < 4; ++j) kreg[j] = *(const u32x4 *)(src + 16 * j);
+    } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kreg[j] = u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int j = 0; j < 4; ++j) kreg[j] = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int key = kt + 4 * vkg + j;
-      if (key < kend)
-        vreg[j] = *(const u32x4 *)(vpool + row_off(key) + vdch * 16);
+      if (pv[j] >= 0)
+        vreg[j] = *(const u32x4 *)(vpool + row_off(pv[j], kt + 4 * vkg + j) + vdch * 16);
       else
         vreg[j] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -108,26 +119,35 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(AttnArgs a) {
   // V key order inside a 16-key group of an LDS row: keys 0-3, 8-11, 4-7, 12-15,
   // so lane half h reads keys {4h..4h+3, 8+4h..8+4h+3} as one 16-byte vector.
   const int vslot = (vkg >> 2) * 16 + (vkg & 1) * 8 + ((vkg >> 1) & 1) * 4;
-  auto stage = [&]() {
+  auto stage = [&](int b) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4 *)&Ks[kkey * KS + kpart * 32 + 8 * j] = kreg[j];
+    for (int j = 0; j < 4; ++j) *(u32x4 *)&Ks[b][kkey * KS + kpart * 32 + 8 * j] = kreg[j];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int w = c >> 1;
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    for (int cc = 0; cc < 8; ++cc) {
+      const int w = cc >> 1;
+      const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
       u32x2 t;
       t[0] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
       t[1] = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
-      *(u32x2 *)&Vt[(8 * vdch + c) * VS + vslot] = t;
+      *(u32x2 *)&Vt[b][(8 * vdch + cc) * VS + vslot] = t;
     }
   };
 
-  gather(it.kbeg);
-  for (int kt = it.kbeg; kt < kend; kt += BN) {
-    __syncthreads();
-    stage();
-    __syncthreads();
-    if (kt + BN < kend) gather(kt + BN);
+  // ---- prologue: step 0 staged, step 1 in registers, ids of step 2 requested
+  fetch_ids(kbeg);
+  gather(kbeg);
+  stage(0);
+  if (nsteps > 1) {
+    fetch_ids(kbeg + BN);
+    gather(kbeg + BN);
+  }
+  if (nsteps > 2) fetch_ids(kbeg + 2 * BN);
+  __syncthreads();
+
+  for (int t = 0; t < nsteps; ++t) {
+    const int kt = kbeg + t * BN;
+    const uint16_t *Kb = Ks[t & 1];
+    const uint16_t *Vb = Vt[t & 1];
 
     // ---- S^T = K Q^T: lane holds keys kt + 32*kb + (i/4)*8 + 4*half + i%4 of row m
     f32x16 s[2];
@@ -137,31 +157,38 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(AttnArgs a) {
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const bf16x8 kf = as_bf16x8(*(const u32x4 *)&Ks[(kb * 32 + q32) * KS + 16 * st + 8 * half]);
+        const bf16x8 kf = as_bf16x8(*(const u32x4 *)&Kb[(kb * 32 + q32) * KS + 16 * st + 8 * half]);
         s[kb] = mfma32(kf, qf[st], s[kb]);
       }
     }
 
-    // ---- online softmax (base 2)
-    const bool need_mask = (kt + BN - 1 > amin) || (kt + BN > kend);
-    const int lim = min(kend - 1, apos);
+    // ---- online softmax, base 2, scale folded into one FMA per logit
+    if ((kt + BN - 1 > amin) || (kt + BN > kend)) {
+      const int lim = min(kend - 1, apos);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt + 32 * kb + (i >> 2) * 8 + 4 * half + (i & 3);
+          s[kb][i] = key <= lim ? s[kb][i] : kNegInf;
+        }
+    }
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = s[kb][i] * a.scale_log2;
-        if (need_mask) {
-          const int key = kt + 32 * kb + (i >> 2) * 8 + 4 * half + (i & 3);
-          v = key <= lim ? v : kNegInf;
-        }
-        s[kb][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float mn = fmaxf(mrun, mx);
-    const float mu = mn == kNegInf ? 0.f : mn;
-    const float al = fast_exp2(mrun - mu);
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
+    mx = fmaxf(mx, shfl_xor(mx, 32)) * c;
+    const bool upd = mx > mref + 8.f;
+    if (upd) {
+      const float al = fast_exp2(mref - mx);  // 0 on the first update
+      lrun *= al;
+      mref = mx;
+      // scale this lane's O rows; lanes without an update keep theirs
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = o[db] * al;
+    }
+    const float mu = mref == kNegInf ? 0.f : mref;
     float sum = 0.f;
     bf16x8 pf[2][2];
 #pragma unroll
@@ -171,17 +198,14 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(AttnArgs a) {
         u32x4 w;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 = fast_exp2(s[kb][8 * s2 + 2 * j] - mu);
-          const float p1 = fast_exp2(s[kb][8 * s2 + 2 * j + 1] - mu);
+          const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * s2 + 2 * j], c, -mu));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * s2 + 2 * j + 1], c, -mu));
           sum += p0 + p1;
           w[j] = pack_bf16x2(p0, p1);
         }
         pf[kb][s2] = as_bf16x8(w);
       }
-    lrun = lrun * al + sum;
-    mrun = mn;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = o[db] * al;
+    lrun += sum;
 
     // ---- O^T += V^T P^T
 #pragma unroll
@@ -191,9 +215,15 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const bf16x8 vf = as_bf16x8(
-              *(const u32x4 *)&Vt[(32 * db + q32) * VS + kb * 32 + s2 * 16 + half * 8]);
+              *(const u32x4 *)&Vb[(32 * db + q32) * VS + kb * 32 + s2 * 16 + half * 8]);
           o[db] = mfma32(vf, pf[kb][s2], o[db]);
         }
+
+    // ---- pipeline: stage step t+1, gather step t+2, request ids of step t+3
+    if (t + 1 < nsteps) stage((t + 1) & 1);
+    if (t + 2 < nsteps) gather(kt + 2 * BN);
+    if (t + 3 < nsteps) fetch_ids(kt + 3 * BN);
+    __syncthreads();
   }
 
   // ---- epilogue: this lane holds channels 32*db + (i/4)*8 + 4*half + i%4 of row m
@@ -223,7 +253,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(AttnArgs a) {
         for (int j = 0; j < 4; ++j) w[j] = o[db][4 * g4 + j] * inv;
         *(f32x4 *)(prow + 32 * db + 8 * g4 + 4 * half) = w;
       }
-    if (half == 0) a.lse_part[pi * a.Hq + qh] = l > 0.f ? mrun + fast_log2(l) : kNegInf;
+    if (half == 0) a.lse_part[pi * a.Hq + qh] = l > 0.f ? mref + fast_log2(l) : kNegInf;
   }
 }
 

@@ -47,8 +47,9 @@ int launch_store_kv(const void *k, const void *v, const int32_t *slots, int64_t 
 // (base 2, of scaled logits) and normalised output o_s,
 //   out = sum_s 2^(l_s - M) o_s / sum_s 2^(l_s - M),  M = max_s l_s,
 // which is the softmax over the union of the key sets (SGLang walkthrough 3.3).
-// A partial with l_s = -inf carries no weight.  One workgroup per merged token;
-// each wavefront takes query heads in turn, each lane D/64 channels.
+// A partial with l_s = -inf carries no weight.  One wavefront per (token, head):
+// lane s holds partial s's weight (64 partials per pass), each lane D/64
+// channels; the partial rows are independent loads issued back to back.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const int32_t *__restrict__ merge,
                                                     const float *__restrict__ o_part,
@@ -56,37 +57,58 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t *__restrict__ 
                                                     void *__restrict__ out, int32_t Hq,
                                                     int32_t dtype) {
   constexpr int PER = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + wave;
+  if (h >= Hq) return;
   const int32_t tok = merge[blockIdx.x * 3 + 0];
   const int32_t pb = merge[blockIdx.x * 3 + 1];
   const int32_t ns = merge[blockIdx.x * 3 + 2];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int h = wave; h < Hq; h += 4) {
-    float M = kNegInf;
-    for (int s = lane; s < ns; s += 64) M = fmaxf(M, lse_part[(int64_t)(pb + s) * Hq + h]);
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
-    float acc[PER];
+  float M = kNegInf;
+  for (int s0 = 0; s0 < ns; s0 += 64)
+    if (s0 + lane < ns) M = fmaxf(M, lse_part[(int64_t)(pb + s0 + lane) * Hq + h]);
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
+  float acc[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-    float W = 0.f;
-    if (M != kNegInf) {
-      for (int s = 0; s < ns; ++s) {
-        const float l = lse_part[(int64_t)(pb + s) * Hq + h];
-        const float w = fast_exp2(l - M);  // exp2(-inf) = 0
-        W += w;
-        const float *op = o_part + ((int64_t)(pb + s) * Hq + h) * D + lane * PER;
+  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  float W = 0.f;
+  if (M != kNegInf) {
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+      const int cnt = min(64, ns - s0);
+      const float lv = lane < cnt ? lse_part[(int64_t)(pb + s0 + lane) * Hq + h] : kNegInf;
+      const float wl = fast_exp2(lv - M);  // 2^-inf = 0
+      W += wl;
+      const float *op = o_part + ((int64_t)(pb + s0) * Hq + h) * D + lane * PER;
+      const int64_t stride = (int64_t)Hq * D;
+      int s = 0;
+      for (; s + 4 <= cnt; s += 4) {
+        float v[4][PER];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] += w * op[j];
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int j = 0; j < PER; ++j) v[u][j] = op[(s + u) * stride + j];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = __shfl(wl, s + u, 64);
+#pragma unroll
+          for (int j = 0; j < PER; ++j) acc[j] += w * v[u][j];
+        }
+      }
+      for (; s < cnt; ++s) {
+        const float w = __shfl(wl, s, 64);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] += w * op[s * stride + j];
       }
     }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
-    const int64_t ob = ((int64_t)tok * Hq + h) * D + lane * PER;
-    if (dtype == RPKV_F32) {
+    for (int off = 32; off > 0; off >>= 1) W += shfl_xor(W, off);
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  const int64_t ob = ((int64_t)tok * Hq + h) * D + lane * PER;
+  if (dtype == RPKV_F32) {
 #pragma unroll
-      for (int j = 0; j < PER; ++j) ((float *)out)[ob + j] = acc[j] * inv;
-    } else {
+    for (int j = 0; j < PER; ++j) ((float *)out)[ob + j] = acc[j] * inv;
+  } else {
 #pragma unroll
-      for (int j = 0; j < PER; ++j) ((uint16_t *)out)[ob + j] = f32_to_bf16(acc[j] * inv);
-    }
+    for (int j = 0; j < PER; ++j) ((uint16_t *)out)[ob + j] = f32_to_bf16(acc[j] * inv);
   }
 }
 
@@ -94,12 +116,13 @@ int launch_merge(const int32_t *merge, int32_t n_merge, const float *o_part,
                  const float *lse_part, void *out, int32_t Hq, int32_t D, int32_t dtype,
                  void *stream) {
   if (n_merge <= 0) return 0;
+  const dim3 grid(n_merge, (Hq + 3) / 4);
   if (D == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(n_merge), dim3(256), 0, (hipStream_t)stream, merge,
-                       o_part, lse_part, out, Hq, dtype);
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, (hipStream_t)stream, merge, o_part,
+                       lse_part, out, Hq, dtype);
   else
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(n_merge), dim3(256), 0, (hipStream_t)stream, merge,
-                       o_part, lse_part, out, Hq, dtype);
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, (hipStream_t)stream, merge, o_part,
+                       lse_part, out, Hq, dtype);
   return (int)hipGetLastError();
 }
 
