@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=LAYERS,
+                    help="layers per step (a model has 32; fewer only for short profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
@@ -155,20 +157,21 @@ def main():
 
     torch.cuda.set_device(0)
     cid, desc = WORKLOADS[args.workload]
+    layers = args.layers
     spec = synth.full_config(cid)
     stream = torch.cuda.current_stream()
 
     # per-layer buffers: q/k/v/out per layer, pools cycled over npools sets
     layer0 = H.device_contents(spec, seed=2024)
     pool_bytes = 2 * layer0.kpool.numel() * layer0.kpool.element_size()
-    npools = int(min(LAYERS, max(2, math.ceil(2e9 / pool_bytes))))
+    npools = int(min(layers, max(2, math.ceil(2e9 / pool_bytes))))
     pools = [(layer0.kpool, layer0.vpool)]
     for j in range(1, npools):
         d = H.device_contents(spec, seed=2024 + j)
         pools.append((d.kpool, d.vpool))
         del d
     qkv = [(layer0.q, layer0.k, layer0.v)]
-    nq = min(LAYERS, 8)
+    nq = min(layers, 8)
     for j in range(1, nq):
         g = torch.Generator(device="cuda")
         g.manual_seed(77 + j)
@@ -182,7 +185,7 @@ def main():
 
     def step():
         plan.prepare(spec.cu_q, spec.L, pt, None, spec.groups, stream=stream)
-        for l in range(LAYERS):
+        for l in range(layers):
             kp, vp = pools[l % npools]
             q, k, v = qkv[l % nq]
             plan.forward(q, k, v, sm, kp, vp, outs[l % nq], spec.scale, stream=stream)
@@ -199,7 +202,7 @@ def main():
     info = plan.info()
 
     # second pass over the same steps with HIP events around every launch
-    plan.timing_enable(True, max_launches=8 * LAYERS * args.steps + 64)
+    plan.timing_enable(True, max_launches=8 * layers * args.steps + 64)
     for _ in range(args.steps):
         step()
     times = plan.timing_collect()
@@ -211,10 +214,10 @@ def main():
                   for k, (n, ms) in times.items()}
     decode_heavy = alg["flops_prefill"] == 0 and spec.dtype == "bf16"
     if decode_heavy:
-        metric_value = alg["kv_total"] * LAYERS / (ms_per_step * 1e-3) / 1e9
+        metric_value = alg["kv_total"] * layers / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
     else:
-        metric_value = alg["flops_total"] * LAYERS / (ms_per_step * 1e-3) / 1e12
+        metric_value = alg["flops_total"] * layers / (ms_per_step * 1e-3) / 1e12
         unit = "TFLOP/s"
     # dominant kernel: the one with the largest summed time
     dom = max((k for k in times if times[k][0]), key=lambda k: times[k][1])
@@ -256,16 +259,16 @@ def main():
         "vs_baseline": None,
         "dtype": spec.dtype,
         "data": "synthetic (seeded N(0,1) tensors, seeded page allocation)",
-        "config": {"workload": desc, "layers_per_step": LAYERS, "pool_sets": npools,
+        "config": {"workload": desc, "layers_per_step": layers, "pool_sets": npools,
                    "batch": spec.bs, "tokens": spec.T,
-                   "step": "prepare_metadata + 32 x (store_kv + attend)"},
+                   "step": f"prepare_metadata + {layers} x (store_kv + attend)"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "extra": {
             "per_kernel": per_kernel,
-            "layer_us": round(ms_per_step * 1e3 / LAYERS, 2),
-            "attention_tflops": round(alg["flops_total"] * LAYERS / (ms_per_step * 1e-3) / 1e12, 3),
-            "kv_read_GBps": round(alg["kv_total"] * LAYERS / (ms_per_step * 1e-3) / 1e9, 1),
+            "layer_us": round(ms_per_step * 1e3 / layers, 2),
+            "attention_tflops": round(alg["flops_total"] * layers / (ms_per_step * 1e-3) / 1e12, 3),
+            "kv_read_GBps": round(alg["kv_total"] * layers / (ms_per_step * 1e-3) / 1e9, 1),
             "decode_kernel_GBps": (round(alg["kv_decode"] / (times["decode"][1] / times["decode"][0]
                                                              * 1e-3) / 1e9, 1)
                                    if times["decode"][0] else None),

@@ -5,21 +5,26 @@
 // so every K/V byte staged in LDS feeds G heads.  Each wavefront owns 32 rows.
 //
 // Per 64-key step:
-//  * the workgroup gathers 64 keys through the page table (16 B per thread per
-//    load, coalesced along each 256-byte row) into registers one step ahead,
-//    then writes K to LDS as [key][channel] and V transposed as [channel][key]
-//    (4 keys x 8 channels per thread, transposed in registers), so both MFMA
-//    A operands below are 16-byte LDS reads;
-//  * S^T = K Q^T with 32x32x16 MFMAs (A = K rows, B = the wavefront's Q rows held
-//    in registers): each lane then holds 32 logits of a single query row, so the
-//    row max and sum are in-lane plus one cross-half shuffle;
+//  * the workgroup gathers 64 K rows and 64 V rows of its KV head through the
+//    page table (each thread 64 contiguous bytes of one row of each) one step
+//    ahead into registers, and stores both row-major in LDS (288-byte rows, two
+//    buffers).  When a page holds >= 16 keys the 16 rows a wavefront loads lie in
+//    one page, so the page id is a wave-uniform load and the row addresses are a
+//    scalar base plus a fixed lane offset;
+//  * S^T = K Q^T with 32x32x16 MFMAs (A = K rows from LDS, B = the wavefront's Q
+//    rows held in registers): each lane then holds 32 logits of a single query
+//    row, so the row max and sum are in-lane plus one cross-half shuffle;
 //  * bottom-right causal mask (key <= position of the row's token; "The
 //    attention backend and a reference implementation", "Variable-length, paged
 //    attention with prefixes") only on steps that cross the diagonal or the key
-//    range end; online softmax in base 2 with scale*log2(e) folded in;
-//  * O^T += V^T P^T with 32x32x16 MFMAs; P^T comes straight from the S^T
-//    accumulators (the key order inside the LDS V rows matches the order the
-//    accumulator registers hold).
+//    range end; online softmax in base 2 with scale*log2(e) folded into one FMA;
+//    the O rescale is skipped unless the running max grows by more than 2^8;
+//  * O^T += V^T P^T with 32x32x16 MFMAs: the V^T operand comes from row-major V
+//    through gfx950's transposing LDS read (ds_read_b64_tr_b16: in each group of
+//    16 lanes, lane i receives element i%4 of the 8-byte chunks addressed by
+//    lanes 4j + i/4, j = 0..3), and P^T straight from the S^T accumulators; the
+//    key order the transposed reads produce matches the order the accumulators
+//    hold.
 // A tile writes its final output, or a partial (normalised fp32 O and base-2
 // log-sum-exp) when its key range is one of several (cascade prefix chunks).
 #include "device_common.h"
@@ -29,14 +34,21 @@ namespace rpkv {
 namespace {
 constexpr int D = 128;
 constexpr int BN = kPrefillKeys;  // 64 keys per step
-constexpr int KS = D + 8;         // K LDS row stride (bf16), padded
-constexpr int VS = BN + 8;        // V^T LDS row stride (bf16), padded
+constexpr int RS = D + 16;        // LDS row stride (bf16): 288 B spreads rows over banks
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ __forceinline__ v4i16 tr_read(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16 *)(__attribute__((address_space(3))) void *)p);
+}
 }  // namespace
 
+template <bool BIGPAGE>
 __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(AttnArgs a) {
   // two K/V buffers: step t computes from buffer t%2 while step t+1 is staged
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * RS];
 
   const Item it = a.items[blockIdx.x];
   if (it.ntok == 0) return;
@@ -68,70 +80,56 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(AttnArgs a) {
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  // Running reference max (scaled, base 2) and this lane's part of the row sum.
-  // The reference moves only when the row max passes it by more than 8, so the
-  // exponentials stay <= 2^8 and the O rescale is skipped on most steps.
   float mref = kNegInf, lrun = 0.f;
   const float c = a.scale_log2;
 
-  // ---- loader roles
+  // ---- loader: row lr (wavefront w owns rows 16w..16w+15), 64-byte quarter part
   const int32_t *ptrow = a.page_table + (int64_t)it.req * a.pt_stride;
   const int pmask = (1 << a.log2P) - 1;
-  const int kkey = tid >> 2, kpart = tid & 3;  // K: key, 32-channel quarter
-  const int vkg = tid & 15, vdch = tid >> 4;   // V: keys 4*vkg..+3, channels 8*vdch..+7
+  const int lr = tid >> 2, part = tid & 3;
   const char *kpool = (const char *)a.kpool;
   const char *vpool = (const char *)a.vpool;
   const int kbeg = it.kbeg, kend = it.kend;
   const int nsteps = (kend - kbeg + BN - 1) / BN;
   u32x4 kreg[4], vreg[4];
-  int32_t pk, pv[4];  // page ids of the loader's keys for the next gather (-1: none)
+  int32_t pg;  // page id for the next gather, -1 when none of the rows is valid
 
   auto fetch_ids = [&](int kt) {
-    const int key = kt + kkey;
-    pk = key < kend ? ptrow[key >> a.log2P] : -1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kv = kt + 4 * vkg + j;
-      pv[j] = kv < kend ? ptrow[kv >> a.log2P] : -1;
+    if (BIGPAGE) {
+      const int k0 = kt + 16 * wave;
+      pg = __builtin_amdgcn_readfirstlane(k0 < kend ? ptrow[k0 >> a.log2P] : -1);
+    } else {
+      const int key = kt + lr;
+      pg = key < kend ? ptrow[key >> a.log2P] : -1;
     }
-  };
-  auto row_off = [&](int32_t page, int key) -> int64_t {
-    const int64_t slot = ((int64_t)clamp_page(page, a.num_pages) << a.log2P) + (key & pmask);
-    return (slot * a.Hkv + it.kvh) * (D * 2);
   };
   auto gather = [&](int kt) {
-    if (pk >= 0) {
-      const char *src = kpool + row_off(pk, kt + kkey) + kpart * 64;
+    const int key = kt + lr;
+    if (pg >= 0 && key < kend) {
+      const int64_t slot = ((int64_t)clamp_page(pg, a.num_pages) << a.log2P) + (key & pmask);
+      const int64_t off = (slot * a.Hkv + it.kvh) * (D * 2) + part * 64;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kreg[j] = *(const u32x4 *)(src + 16 * j);
+      for (int j = 0; j < 4; ++j) kreg[j] = *(const u32x4 *)(kpool + off + 16 * j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vreg[j] = *(const u32x4 *)(vpool + off + 16 * j);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kreg[j] = u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (pv[j] >= 0)
-        vreg[j] = *(const u32x4 *)(vpool + row_off(pv[j], kt + 4 * vkg + j) + vdch * 16);
-      else
+      for (int j = 0; j < 4; ++j) {
+        kreg[j] = u32x4{0u, 0u, 0u, 0u};
         vreg[j] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
-  // V key order inside a 16-key group of an LDS row: keys 0-3, 8-11, 4-7, 12-15,
-  // so lane half h reads keys {4h..4h+3, 8+4h..8+4h+3} as one 16-byte vector.
-  const int vslot = (vkg >> 2) * 16 + (vkg & 1) * 8 + ((vkg >> 1) & 1) * 4;
   auto stage = [&](int b) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4 *)&Ks[b][kkey * KS + kpart * 32 + 8 * j] = kreg[j];
+    for (int j = 0; j < 4; ++j) *(u32x4 *)&Ks[b][lr * RS + part * 32 + 8 * j] = kreg[j];
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const int w = cc >> 1;
-      const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-      u32x2 t;
-      t[0] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-      t[1] = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
-      *(u32x2 *)&Vt[b][(8 * vdch + cc) * VS + vslot] = t;
-    }
+    for (int j = 0; j < 4; ++j) *(u32x4 *)&Vs[b][lr * RS + part * 32 + 8 * j] = vreg[j];
   };
+  // transposed V read of this lane: in its 16-lane group g, lane 4j+q points at
+  // key row 4*half + j (+ 8*r) and channels 16*(g%2) + 4q (+ 32*db)
+  const int vg = lane >> 4, vj = (lane & 15) >> 2, vq = lane & 3;
+  const int vbase = (4 * half + vj) * RS + 16 * (vg & 1) + 4 * vq;
 
   // ---- prologue: step 0 staged, step 1 in registers, ids of step 2 requested
   fetch_ids(kbeg);
@@ -147,31 +145,31 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(AttnArgs a) {
   for (int t = 0; t < nsteps; ++t) {
     const int kt = kbeg + t * BN;
     const uint16_t *Kb = Ks[t & 1];
-    const uint16_t *Vb = Vt[t & 1];
+    const uint16_t *Vb = Vs[t & 1];
 
-    // ---- S^T = K Q^T: lane holds keys kt + 32*kb + (i/4)*8 + 4*half + i%4 of row m
+    // ---- S^T = K Q^T: lane holds keys kt + 32*kb + (i/4)*8 + 4*half + i%4 of row m;
+    // two independent accumulation chains (key blocks 0 and 1) interleaved
     f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const bf16x8 kf = as_bf16x8(*(const u32x4 *)&Kb[(kb * 32 + q32) * KS + 16 * st + 8 * half]);
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = as_bf16x8(*(const u32x4 *)&Kb[(kb * 32 + q32) * RS + 16 * st + 8 * half]);
         s[kb] = mfma32(kf, qf[st], s[kb]);
       }
-    }
 
-    // ---- online softmax, base 2, scale folded into one FMA per logit
+    // ---- online softmax, base 2
     if ((kt + BN - 1 > amin) || (kt + BN > kend)) {
-      const int lim = min(kend - 1, apos);
+      const int rel = min(kend - 1, apos) - kt - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kt + 32 * kb + (i >> 2) * 8 + 4 * half + (i & 3);
-          s[kb][i] = key <= lim ? s[kb][i] : kNegInf;
-        }
+        for (int i = 0; i < 16; ++i)
+          s[kb][i] = (32 * kb + (i >> 2) * 8 + (i & 3)) <= rel ? s[kb][i] : kNegInf;
     }
     float mx = kNegInf;
 #pragma unroll
@@ -179,12 +177,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
     mx = fmaxf(mx, shfl_xor(mx, 32)) * c;
-    const bool upd = mx > mref + 8.f;
-    if (upd) {
+    if (mx > mref + 8.f) {
       const float al = fast_exp2(mref - mx);  // 0 on the first update
       lrun *= al;
       mref = mx;
-      // scale this lane's O rows; lanes without an update keep theirs
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] = o[db] * al;
     }
@@ -207,15 +203,18 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(AttnArgs a) {
       }
     lrun += sum;
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T (V^T through the transposing LDS read)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const bf16x8 vf = as_bf16x8(
-              *(const u32x4 *)&Vb[(32 * db + q32) * VS + kb * 32 + s2 * 16 + half * 8]);
+          const uint16_t *vp = Vb + vbase + (kb * 32 + s2 * 16) * RS + 32 * db;
+          const v4i16 lo = tr_read(vp);
+          const v4i16 hi = tr_read(vp + 8 * RS);
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = mfma32(vf, pf[kb][s2], o[db]);
         }
 
@@ -259,8 +258,15 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(AttnArgs a) {
 
 int launch_prefill_bf16(const AttnArgs &a, void *stream) {
   if (a.n_items <= 0) return 0;
-  hipLaunchKernelGGL(attn_prefill_bf16_kernel, dim3(a.n_items), dim3(256), 0, (hipStream_t)stream,
-                     a);
+  // pages of >= 16 keys: a wavefront's 16 rows of a step share one page (steps
+  // start on multiples of 64 keys: tiles start at key 0, cascade chunks at
+  // multiples of 64)
+  if (a.log2P >= 4)
+    hipLaunchKernelGGL(attn_prefill_bf16_kernel<true>, dim3(a.n_items), dim3(256), 0,
+                       (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(attn_prefill_bf16_kernel<false>, dim3(a.n_items), dim3(256), 0,
+                       (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

@@ -96,7 +96,7 @@ rpkv_status check_shape(const rpkv_shape *s, Shape *o, std::string *msg) {
   o->max_tokens = s->max_tokens;
   o->decode_max_rows = s->decode_max_rows ? s->decode_max_rows : kDecodeRows;
   o->split_target = s->split_target ? s->split_target : 8192;
-  o->split_min_keys = (int32_t)round_up(s->split_min_keys ? s->split_min_keys : 256, kDecodeKeys);
+  o->split_min_keys = (int32_t)round_up(s->split_min_keys ? s->split_min_keys : 64, kDecodeKeys);
   return RPKV_OK;
 }
 
@@ -314,8 +314,10 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
     const int32_t n = n_of(i);
     const int32_t ns = (int32_t)cdiv(L[i], chunk);
     for (int32_t t = cu[i]; t < cu[i + 1]; ++t) nsplit[t] = ns;
-    for (int32_t h = 0; h < s.Hkv; ++h)
-      for (int32_t c = 0; c < ns; ++c)
+    // KV heads innermost: the heads of one chunk read interleaved rows of the
+    // same pages at about the same time
+    for (int32_t c = 0; c < ns; ++c)
+      for (int32_t h = 0; h < s.Hkv; ++h)
         dec.push_back(Item{i, h, cu[i], n, L[i] - n, c * chunk, std::min(L[i], (c + 1) * chunk),
                            ns > 1 ? c : -1});
   }
@@ -359,8 +361,8 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
       const int32_t n = n_of(j);
       const int32_t ns = (int32_t)cdiv(L[j] - prefix, chunk);
       for (int32_t t = cu[j]; t < cu[j + 1]; ++t) nsplit[t] = (int32_t)npc + ns;
-      for (int32_t h = 0; h < s.Hkv; ++h)
-        for (int32_t c = 0; c < ns; ++c)
+      for (int32_t c = 0; c < ns; ++c)
+        for (int32_t h = 0; h < s.Hkv; ++h)
           dec.push_back(Item{j, h, cu[j], n, L[j] - n, prefix + c * chunk,
                              std::min(L[j], prefix + (c + 1) * chunk), (int32_t)npc + c});
       ++p.cascade_members;
