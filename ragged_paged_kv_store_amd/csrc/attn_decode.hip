@@ -30,11 +30,6 @@ namespace {
 
 constexpr int D = 128;
 
-struct Slots {
-  int32_t k[2];  // pool slots of this lane's two K rows (key blocks 0 and 1)
-  int32_t v[8];  // pool slots of this lane's eight V rows
-};
-
 struct Regs {
   u32x4 k[2][4];
   u32x4 v[8];
@@ -42,8 +37,22 @@ struct Regs {
 
 // Keys of one 32-key step held by this lane:
 //  K (A operand of S^T): key kb + 16*sb + col for sb = 0, 1
-//  V (A operand of O^T): key kb + 4*grp + e (e < 4), kb + 16 + 4*grp + (e - 4)
-// Keys at or past kend are clamped to kend - 1 (always readable) and masked.
+//  V (A operand of O^T): key kb + 16*(e/4) + 4*grp + e%4, e = 0..7
+//
+// Small pages (< 16 keys): every key's slot is looked up; keys at or past kend
+// are clamped to kend - 1 (always readable) and masked.
+struct SlotsSmall {
+  int32_t k[2];
+  int32_t v[8];
+};
+// Pages of >= 16 keys: steps start on multiples of 16 keys, so keys
+// kb..kb+15 and kb+16..kb+31 each lie in one page; the two page ids are
+// wave-uniform.  Keys past the range read in-page rows (their page index is
+// clamped to the last page in range) and are masked; their V rows are zeroed.
+struct SlotsBig {
+  int32_t pg[2];
+};
+
 __device__ __forceinline__ int32_t slot_of(const int32_t *ptrow, int key, int kend, int log2P,
                                            int64_t num_pages) {
   const int kc = key < kend ? key : kend - 1;
@@ -56,8 +65,8 @@ __device__ __forceinline__ int64_t row_bytes_off(int32_t slot, int hkv, int kvh)
   return ((int64_t)(uint32_t)slot * hkv + kvh) * (D * 2);
 }
 
-__device__ __forceinline__ void lookup(Slots &s, const int32_t *ptrow, int kb, int kend, int col,
-                                       int grp, int log2P, int64_t num_pages) {
+__device__ __forceinline__ void lookup(SlotsSmall &s, const int32_t *ptrow, int kb, int kend,
+                                       int col, int grp, int log2P, int64_t num_pages) {
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) s.k[sb] = slot_of(ptrow, kb + 16 * sb + col, kend, log2P, num_pages);
 #pragma unroll
@@ -67,8 +76,19 @@ __device__ __forceinline__ void lookup(Slots &s, const int32_t *ptrow, int kb, i
   }
 }
 
-__device__ __forceinline__ void load(Regs &r, const Slots &s, const char *kpool,
-                                     const char *vpool, int col, int grp, int hkv, int kvh) {
+__device__ __forceinline__ void lookup(SlotsBig &s, const int32_t *ptrow, int kb, int kend, int,
+                                       int, int log2P, int64_t num_pages) {
+  const int last = (kend - 1) >> log2P;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const int pi = min((kb + 16 * sb) >> log2P, last);
+    s.pg[sb] = __builtin_amdgcn_readfirstlane(clamp_page(ptrow[pi], num_pages));
+  }
+}
+
+__device__ __forceinline__ void load(Regs &r, const SlotsSmall &s, const char *kpool,
+                                     const char *vpool, int, int col, int grp, int, int hkv,
+                                     int kvh) {
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -80,13 +100,31 @@ __device__ __forceinline__ void load(Regs &r, const Slots &s, const char *kpool,
     r.v[e] = *(const u32x4 *)(vpool + row_bytes_off(s.v[e], hkv, kvh) + col * 16);
 }
 
+__device__ __forceinline__ void load(Regs &r, const SlotsBig &s, const char *kpool,
+                                     const char *vpool, int kb, int col, int grp, int log2P,
+                                     int hkv, int kvh) {
+  const int pmask = (1 << log2P) - 1;
+  const int64_t rowb = (int64_t)hkv * (D * 2);  // bytes between consecutive slots
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    // first slot of this 16-key block, then this lane's row within it
+    const int32_t s0 = (s.pg[sb] << log2P) + ((kb + 16 * sb) & pmask);
+    const char *kbase = kpool + row_bytes_off(s0, hkv, kvh) + (int64_t)col * rowb;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) r.k[sb][st] = *(const u32x4 *)(kbase + (st * 32 + grp * 8) * 2);
+    const char *vbase = vpool + row_bytes_off(s0, hkv, kvh) + (int64_t)(4 * grp) * rowb + col * 16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r.v[4 * sb + e] = *(const u32x4 *)(vbase + e * rowb);
+  }
+}
+
 struct State {
   f32x4 o[8];
   float m, l;
 };
 
-__device__ __forceinline__ void step(State &st, const Regs &r, const bf16x8 (&qf)[4], int kb,
-                                     int kend, int apos, int grp, float scale_log2) {
+__device__ __forceinline__ void step(State &st, Regs &r, const bf16x8 (&qf)[4], int kb, int kend,
+                                     int apos, int grp, float scale_log2) {
   f32x4 s[2];
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
@@ -94,21 +132,27 @@ __device__ __forceinline__ void step(State &st, const Regs &r, const bf16x8 (&qf
 #pragma unroll
     for (int t = 0; t < 4; ++t) s[sb] = mfma16(as_bf16x8(r.k[sb][t]), qf[t], s[sb]);
   }
+  if (kb + 32 > kend) {
+    // last step of the chunk: V rows of keys past the range must not reach the
+    // product (their P is 0, but an unreferenced row may hold anything)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (kb + (e >> 2) * 16 + 4 * grp + (e & 3) >= kend) r.v[e] = u32x4{0u, 0u, 0u, 0u};
+  }
   // this lane holds column col's logits for keys kb + 16*sb + 4*grp + i
-  const int lim = min(kend - 1, apos);
+  const int rel = min(kend - 1, apos) - kb - 4 * grp;
   float x[8];
   float mx = kNegInf;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = kb + 16 * sb + 4 * grp + i;
-      const float v = key <= lim ? s[sb][i] * scale_log2 : kNegInf;
+      const float v = (16 * sb + i) <= rel ? s[sb][i] : kNegInf;
       x[sb * 4 + i] = v;
       mx = fmaxf(mx, v);
     }
   mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
+  mx = fmaxf(mx, shfl_xor(mx, 32)) * scale_log2;
   const float mn = fmaxf(st.m, mx);
   const float mu = mn == kNegInf ? 0.f : mn;
   const float al = fast_exp2(st.m - mu);
@@ -116,7 +160,7 @@ __device__ __forceinline__ void step(State &st, const Regs &r, const bf16x8 (&qf
   float sum = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    p[e] = fast_exp2(x[e] - mu);
+    p[e] = fast_exp2(__builtin_fmaf(x[e], scale_log2, -mu));
     sum += p[e];
   }
   st.l = st.l * al + sum;
@@ -145,7 +189,8 @@ __device__ __forceinline__ void step(State &st, const Regs &r, const bf16x8 (&qf
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void attn_decode_bf16_kernel(AttnArgs a) {
+template <class Slots>
+__global__ __launch_bounds__(256, 2) void attn_decode_bf16_kernel(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ii = blockIdx.x * kDecodeWavesPerBlock + wave;
   if (ii >= a.n_items) return;
@@ -180,21 +225,23 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(AttnArgs a) {
   const char *kp = (const char *)a.kpool;
   const char *vp = (const char *)a.vpool;
   const int kend = it.kend;
+  const int L2 = a.log2P;
   Slots sa, sb;
   Regs ra, rb;
-  lookup(sa, ptrow, it.kbeg, kend, col, grp, a.log2P, a.num_pages);
-  load(ra, sa, kp, vp, col, grp, a.Hkv, it.kvh);
+  lookup(sa, ptrow, it.kbeg, kend, col, grp, L2, a.num_pages);
+  load(ra, sa, kp, vp, it.kbeg, col, grp, L2, a.Hkv, it.kvh);
   if (it.kbeg + kDecodeKeys < kend)
-    lookup(sb, ptrow, it.kbeg + kDecodeKeys, kend, col, grp, a.log2P, a.num_pages);
+    lookup(sb, ptrow, it.kbeg + kDecodeKeys, kend, col, grp, L2, a.num_pages);
   for (int kb = it.kbeg; kb < kend; kb += 2 * kDecodeKeys) {
-    if (kb + kDecodeKeys < kend) load(rb, sb, kp, vp, col, grp, a.Hkv, it.kvh);
+    if (kb + kDecodeKeys < kend) load(rb, sb, kp, vp, kb + kDecodeKeys, col, grp, L2, a.Hkv, it.kvh);
     if (kb + 2 * kDecodeKeys < kend)
-      lookup(sa, ptrow, kb + 2 * kDecodeKeys, kend, col, grp, a.log2P, a.num_pages);
+      lookup(sa, ptrow, kb + 2 * kDecodeKeys, kend, col, grp, L2, a.num_pages);
     step(st, ra, qf, kb, kend, apos, grp, a.scale_log2);
     if (kb + kDecodeKeys >= kend) break;
-    if (kb + 2 * kDecodeKeys < kend) load(ra, sa, kp, vp, col, grp, a.Hkv, it.kvh);
+    if (kb + 2 * kDecodeKeys < kend)
+      load(ra, sa, kp, vp, kb + 2 * kDecodeKeys, col, grp, L2, a.Hkv, it.kvh);
     if (kb + 3 * kDecodeKeys < kend)
-      lookup(sb, ptrow, kb + 3 * kDecodeKeys, kend, col, grp, a.log2P, a.num_pages);
+      lookup(sb, ptrow, kb + 3 * kDecodeKeys, kend, col, grp, L2, a.num_pages);
     step(st, rb, qf, kb + kDecodeKeys, kend, apos, grp, a.scale_log2);
   }
 
@@ -235,8 +282,14 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(AttnArgs a) {
 int launch_decode_bf16(const AttnArgs &a, void *stream) {
   if (a.n_items <= 0) return 0;
   const int blocks = (a.n_items + kDecodeWavesPerBlock - 1) / kDecodeWavesPerBlock;
-  hipLaunchKernelGGL(attn_decode_bf16_kernel, dim3(blocks), dim3(64 * kDecodeWavesPerBlock), 0,
-                     (hipStream_t)stream, a);
+  // pages of >= 16 keys: 16-key blocks of a step lie in one page (chunks start
+  // on multiples of 32 keys or at a cascade prefix length, a multiple of the page)
+  if (a.log2P >= 4)
+    hipLaunchKernelGGL(attn_decode_bf16_kernel<SlotsBig>, dim3(blocks),
+                       dim3(64 * kDecodeWavesPerBlock), 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(attn_decode_bf16_kernel<SlotsSmall>, dim3(blocks),
+                       dim3(64 * kDecodeWavesPerBlock), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

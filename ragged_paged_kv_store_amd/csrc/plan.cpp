@@ -322,16 +322,46 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
                            ns > 1 ? c : -1});
   }
 
-  // prefill-type requests
+  // prefill-type requests: tiles of tpt tokens x G heads of one KV head
+  std::vector<Item> tiles;
+  std::vector<int64_t> tile_key;
+  int64_t total_steps = 0;
   for (int32_t i = 0; i < batch; ++i) {
     const int32_t n = n_of(i);
     if (n == 0 || is_decode(i)) continue;
     for (int32_t h = 0; h < s.Hkv; ++h)
       for (int32_t r0 = 0; r0 < n; r0 += tpt) {
         const int32_t r1 = std::min(n, r0 + tpt);
-        pre.push_back(Item{i, h, cu[i] + r0, r1 - r0, L[i] - n + r0, 0, L[i] - n + r1, -1});
-        pre_key.push_back((int64_t)i * s.Hkv + h);
+        tiles.push_back(Item{i, h, cu[i] + r0, r1 - r0, L[i] - n + r0, 0, L[i] - n + r1, -1});
+        tile_key.push_back((int64_t)i * s.Hkv + h);
+        total_steps += cdiv(L[i] - n + r1, kPrefillKeys);
       }
+  }
+  // A tile much longer than the fair share of steps per concurrent tile slot
+  // would set the launch's critical path: cut its key range into pieces of whole
+  // 64-key steps, merged afterwards like split-KV chunks.  (Not for fp32.)
+  const int64_t fair = std::max<int64_t>(8, cdiv(total_steps, kPrefillSlots));
+  for (size_t k = 0; k < tiles.size(); ++k) {
+    const Item &t = tiles[k];
+    const int64_t steps = cdiv(t.kend, kPrefillKeys);
+    int64_t parts = f32 ? 1 : cdiv(steps, fair);
+    if (steps <= fair + fair / 2) parts = 1;
+    if (parts <= 1) {
+      pre.push_back(t);
+      pre_key.push_back(tile_key[k]);
+      continue;
+    }
+    const int64_t per = cdiv(steps, parts) * kPrefillKeys;
+    parts = cdiv(t.kend, per);
+    for (int32_t tk = t.tok0; tk < t.tok0 + t.ntok; ++tk) nsplit[tk] = (int32_t)parts;
+    for (int64_t pc = 0; pc < parts; ++pc) {
+      Item piece = t;
+      piece.kbeg = (int32_t)(pc * per);
+      piece.kend = (int32_t)std::min<int64_t>(t.kend, (pc + 1) * per);
+      piece.split = (int32_t)pc;
+      pre.push_back(piece);
+      pre_key.push_back(tile_key[k]);
+    }
   }
 
   // cascade groups

@@ -37,6 +37,7 @@ constexpr int kDecodeWavesPerBlock = 4;
 constexpr int kF32Rows = 16;          // fp32 tile rows
 constexpr int kF32Keys = 32;          // fp32 keys per LDS tile
 constexpr int kNumXcd = 8;            // MI355X: 8 XCDs, blocks go round-robin
+constexpr int kPrefillSlots = 512;    // MI355X: 256 CUs x 2 resident prefill tiles
 
 struct HostPlan {
   int32_t batch = 0, T = 0, max_q = 0, max_k = 0;
