@@ -223,7 +223,9 @@ def main():
     dom = max((k for k in times if times[k][0]), key=lambda k: times[k][1])
     n_l, ms_l = times[dom]
     avg_s = ms_l / n_l * 1e-3
-    if dom == "prefill":
+    if dom in ("prefill", "fused"):
+        # the fused launch also streams the split-KV chunks; only the tiles'
+        # algorithmic FLOPs are credited
         roof = dict(bound="mfma", achieved=alg["flops_prefill"] / avg_s / 1e12,
                     peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
     elif dom == "decode":
@@ -272,6 +274,7 @@ def main():
             "decode_kernel_GBps": (round(alg["kv_decode"] / (times["decode"][1] / times["decode"][0]
                                                              * 1e-3) / 1e9, 1)
                                    if times["decode"][0] else None),
+            "split_kv_in_fused_launch": bool(times.get("fused", (0, 0))[0]),
             "algorithmic_per_layer": alg,
             "plan": info,
         },

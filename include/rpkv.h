@@ -90,7 +90,7 @@ typedef struct rpkv_shape {
                                 launch when choosing split-KV chunks (default
                                 8192)                                           */
   int32_t split_min_keys;    /* tuning: smallest split-KV chunk in keys
-                                (default 256; rounded up to 32)                 */
+                                (default 64; rounded up to 32)                  */
 } rpkv_shape;
 
 /* Cascade hint: requests [first_req, first_req + num_reqs) of the batch have
@@ -132,7 +132,9 @@ typedef enum rpkv_kernel_kind {
   RPKV_KERNEL_DECODE = 2,  /* bf16 split-KV                         */
   RPKV_KERNEL_MERGE = 3,   /* log-sum-exp merge                     */
   RPKV_KERNEL_F32 = 4,     /* fp32 tiles                            */
-  RPKV_KERNEL_KINDS = 5
+  RPKV_KERNEL_FUSED = 5,   /* split-KV chunks and MFMA tiles in one
+                              launch (mixed bf16 batches)           */
+  RPKV_KERNEL_KINDS = 6
 } rpkv_kernel_kind;
 
 typedef struct rpkv_kernel_times {

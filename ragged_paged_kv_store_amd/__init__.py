@@ -25,7 +25,7 @@ STATUS = {0: "RPKV_OK", 1: "RPKV_ERR_INVALID_ARG", 2: "RPKV_ERR_UNSUPPORTED",
           3: "RPKV_ERR_WORKSPACE_TOO_SMALL", 4: "RPKV_ERR_NOT_PREPARED", 5: "RPKV_ERR_HIP",
           6: "RPKV_ERR_CAPACITY"}
 BF16, F32 = 0, 1
-KERNEL_KINDS = ("store", "prefill", "decode", "merge", "f32")
+KERNEL_KINDS = ("store", "prefill", "decode", "merge", "f32", "fused")
 
 # every function include/rpkv.h declares
 EXPORTS = (

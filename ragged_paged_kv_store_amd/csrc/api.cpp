@@ -378,10 +378,13 @@ rpkv_status rpkv_attend(rpkv_plan *p, const void *q, const void *kpool, const vo
   dec.n_items = (int32_t)hp.decode.size();
   rpkv_status st = RPKV_OK;
   if (p->s.dtype == RPKV_BF16) {
-    if (pre.n_items > 0)
+    if (pre.n_items > 0 && dec.n_items > 0)
+      st = timed(p, RPKV_KERNEL_FUSED, stream,
+                 [&] { return rpkv::launch_fused_bf16(pre, dec, stream); }, "fused launch");
+    else if (pre.n_items > 0)
       st = timed(p, RPKV_KERNEL_PREFILL, stream, [&] { return rpkv::launch_prefill_bf16(pre, stream); },
                  "prefill launch");
-    if (st == RPKV_OK && dec.n_items > 0)
+    else if (dec.n_items > 0)
       st = timed(p, RPKV_KERNEL_DECODE, stream, [&] { return rpkv::launch_decode_bf16(dec, stream); },
                  "decode launch");
   } else {

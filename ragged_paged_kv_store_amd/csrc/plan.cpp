@@ -293,34 +293,9 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
     }
   }
 
-  // split-KV chunk: one length for the batch, sized for ~split_target items
-  int64_t dec_keys = 0;
-  for (int32_t i = 0; i < batch; ++i) {
-    if (!is_decode(i)) continue;
-    dec_keys += (int64_t)(is_member[i] ? L[i] - groups[in_group[i]].prefix_len : L[i]) * s.Hkv;
-  }
-  const int64_t chunk64 =
-      std::max<int64_t>(s.split_min_keys, round_up(cdiv(dec_keys, s.split_target), kDecodeKeys));
-  const int32_t chunk = (int32_t)std::min<int64_t>(chunk64, 1 << 30);
-  p.decode_chunk = chunk;
-
   std::vector<int32_t> nsplit(T, 1);
   std::vector<Item> pre, dec;
   std::vector<int64_t> pre_key;  // K/V-sharing group key per prefill item
-
-  // decode-type requests outside any cascade
-  for (int32_t i = 0; i < batch; ++i) {
-    if (!is_decode(i) || is_member[i]) continue;
-    const int32_t n = n_of(i);
-    const int32_t ns = (int32_t)cdiv(L[i], chunk);
-    for (int32_t t = cu[i]; t < cu[i + 1]; ++t) nsplit[t] = ns;
-    // KV heads innermost: the heads of one chunk read interleaved rows of the
-    // same pages at about the same time
-    for (int32_t c = 0; c < ns; ++c)
-      for (int32_t h = 0; h < s.Hkv; ++h)
-        dec.push_back(Item{i, h, cu[i], n, L[i] - n, c * chunk, std::min(L[i], (c + 1) * chunk),
-                           ns > 1 ? c : -1});
-  }
 
   // prefill-type requests: tiles of tpt tokens x G heads of one KV head
   std::vector<Item> tiles;
@@ -364,7 +339,8 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
     }
   }
 
-  // cascade groups
+  // cascade prefix tiles: all eligible members' rows against the shared keys
+  std::vector<int32_t> casc_npc(ngroups, 0);
   for (int32_t g = 0; g < ngroups; ++g) {
     if (casc[g].empty()) continue;
     const int32_t prefix = groups[g].prefix_len;
@@ -378,6 +354,7 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
     npc = std::max<int64_t>(1, std::min<int64_t>(npc, prefix / 256));
     const int32_t pchunk = (int32_t)round_up(cdiv(prefix, npc), kPrefillKeys);
     npc = cdiv(prefix, pchunk);
+    casc_npc[g] = (int32_t)npc;
     for (int32_t h = 0; h < s.Hkv; ++h)
       for (int32_t tl = 0; tl < ntile; ++tl)
         for (int32_t c = 0; c < npc; ++c) {
@@ -387,14 +364,59 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
           pre_key.push_back(((int64_t)batch + g) * s.Hkv + h);
           ++p.n_cascade_items;
         }
+  }
+
+  // split-KV chunk: one length for the batch, sized for ~split_target items.
+  // When MFMA tiles share the launch, the chunks run beside them, so a chunk
+  // only has to finish within the tiles' estimated duration: stretch it to what
+  // one wavefront streams in that time (fewer partials to merge).
+  int64_t dec_keys = 0;
+  for (int32_t i = 0; i < batch; ++i) {
+    if (!is_decode(i)) continue;
+    dec_keys += (int64_t)(is_member[i] ? L[i] - groups[in_group[i]].prefix_len : L[i]) * s.Hkv;
+  }
+  int64_t chunk64 =
+      std::max<int64_t>(s.split_min_keys, round_up(cdiv(dec_keys, s.split_target), kDecodeKeys));
+  if (!f32 && !pre.empty()) {
+    int64_t longest = 0, steps_all = 0;
+    for (const Item &it : pre) {
+      const int64_t st = item_work(it);
+      longest = std::max(longest, st);
+      steps_all += st;
+    }
+    const int64_t est_steps = std::max(longest, cdiv(steps_all, kPrefillSlots));
+    chunk64 = std::max(chunk64, round_up(est_steps * kConcurrentKeysPerStep, kDecodeKeys));
+  }
+  const int32_t chunk = (int32_t)std::min<int64_t>(chunk64, 1 << 30);
+  p.decode_chunk = chunk;
+
+  // decode-type requests outside any cascade
+  for (int32_t i = 0; i < batch; ++i) {
+    if (!is_decode(i) || is_member[i]) continue;
+    const int32_t n = n_of(i);
+    const int32_t ns = (int32_t)cdiv(L[i], chunk);
+    for (int32_t t = cu[i]; t < cu[i + 1]; ++t) nsplit[t] = ns;
+    // KV heads innermost: the heads of one chunk read interleaved rows of the
+    // same pages at about the same time
+    for (int32_t c = 0; c < ns; ++c)
+      for (int32_t h = 0; h < s.Hkv; ++h)
+        dec.push_back(Item{i, h, cu[i], n, L[i] - n, c * chunk, std::min(L[i], (c + 1) * chunk),
+                           ns > 1 ? c : -1});
+  }
+
+  // cascade tails: each member's own keys past the prefix
+  for (int32_t g = 0; g < ngroups; ++g) {
+    if (casc[g].empty()) continue;
+    const int32_t prefix = groups[g].prefix_len;
+    const int32_t npc = casc_npc[g];
     for (int32_t j : casc[g]) {
       const int32_t n = n_of(j);
       const int32_t ns = (int32_t)cdiv(L[j] - prefix, chunk);
-      for (int32_t t = cu[j]; t < cu[j + 1]; ++t) nsplit[t] = (int32_t)npc + ns;
+      for (int32_t t = cu[j]; t < cu[j + 1]; ++t) nsplit[t] = npc + ns;
       for (int32_t c = 0; c < ns; ++c)
         for (int32_t h = 0; h < s.Hkv; ++h)
           dec.push_back(Item{j, h, cu[j], n, L[j] - n, prefix + c * chunk,
-                             std::min(L[j], prefix + (c + 1) * chunk), (int32_t)npc + c});
+                             std::min(L[j], prefix + (c + 1) * chunk), npc + c});
       ++p.cascade_members;
     }
   }
