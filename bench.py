@@ -87,6 +87,34 @@ def algorithmic(spec, plan_info_members: int):
                 kv_total=kv_total, bytes_total=kv_total + io, store_bytes=store_bytes)
 
 
+def kernel_sources_hash() -> str:
+    """Hash of the library's kernel and planner sources (as recorded in
+    profiles/traffic.json when the HBM counters were taken)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "ragged_paged_kv_store_amd", "csrc", "*"))):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(os.path.basename(f).encode())
+            h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs (scaled by the copy calibration), or None when
+    there is no such record or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    k = rec.get("kernels", {}).get(workload)
+    if not k or k.get("kernel") != kernel or rec.get("source_hash") != kernel_sources_hash():
+        return None
+    return k["bytes_per_launch"]
+
+
 def cpu_baseline(spec, db, H, budget_flops: float = 40e9):
     """The fp64 oracle as it stands, on the host, over one layer of the batch:
     every row when the layer is within ~40 GFLOP (about 30 core-seconds),
@@ -144,6 +172,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=LAYERS,
                     help="layers per step (a model has 32; fewer only for short profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
+                         "reference that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
@@ -151,11 +182,20 @@ def main():
         sys.exit(2)
 
     import torch
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel(), "launches": 5}))
+        return
+
     import ragged_paged_kv_store_amd as rp
     from tests import gpu_harness as H
     from workloads import synth
 
-    torch.cuda.set_device(0)
     cid, desc = WORKLOADS[args.workload]
     layers = args.layers
     spec = synth.full_config(cid)
@@ -239,7 +279,7 @@ def main():
                     unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = dom
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(args.workload, dom) if layers == LAYERS else None
 
     cpu = None
     if not args.no_cpu_baseline:
