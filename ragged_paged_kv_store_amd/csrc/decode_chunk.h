@@ -195,7 +195,9 @@ __device__ __forceinline__ void step(State &st, Regs &r, const bf16x8 (&qf)[4], 
 template <class Slots>
 __device__ __forceinline__ void decode_chunk(const AttnArgs &a, int block) {
   using namespace dchunk;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // uniform wavefront index: the item and its page ids are then scalar loads,
+  // which do not wait on the vector-load counter of the K/V loads in flight
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int ii = block * kDecodeWavesPerBlock + wave;
   if (ii >= a.n_items) return;
   const Item it = a.items[ii];

@@ -36,7 +36,15 @@ namespace rpkv {
 namespace ptile {
 constexpr int D = 128;
 constexpr int BN = kPrefillKeys;  // 64 keys per step
-constexpr int RS = D + 16;        // LDS row stride (bf16): 288 B spreads rows over banks
+#ifndef VPAD
+#define VPAD 16
+#endif
+// LDS row strides (bf16).  K rows are read 16 lanes x 16 B per pass, one row
+// per lane: 272 B (68 dwords = 4 mod 64) puts 16 consecutive rows on distinct
+// banks.  V rows are read by the transposing read, 4 rows x 32 B per 16-lane
+// group, which wants the row stride apart by a multiple of 8 dwords.
+constexpr int RSK = D + 8;
+constexpr int RSV = D + VPAD;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
@@ -50,12 +58,14 @@ template <bool BIGPAGE>
 __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
   using namespace ptile;
   // two K/V buffers: step t computes from buffer t%2 while step t+1 is staged
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * RSK];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * RSV];
 
   const Item it = a.items[tile];
   if (it.ntok == 0) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wavefront index is uniform; saying so lets per-wave addresses (the page
+  // ids below) be scalar loads that do not wait on the vector-load counter
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int q32 = lane & 31, half = lane >> 5;
   const int G = a.G;
   const int rows = it.ntok * G;
@@ -125,14 +135,14 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
   };
   auto stage = [&](int b) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4 *)&Ks[b][lr * RS + part * 32 + 8 * j] = kreg[j];
+    for (int j = 0; j < 4; ++j) *(u32x4 *)&Ks[b][lr * RSK + part * 32 + 8 * j] = kreg[j];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4 *)&Vs[b][lr * RS + part * 32 + 8 * j] = vreg[j];
+    for (int j = 0; j < 4; ++j) *(u32x4 *)&Vs[b][lr * RSV + part * 32 + 8 * j] = vreg[j];
   };
   // transposed V read of this lane: in its 16-lane group g, lane 4j+q points at
   // key row 4*half + j (+ 8*r) and channels 16*(g%2) + 4q (+ 32*db)
   const int vg = lane >> 4, vj = (lane & 15) >> 2, vq = lane & 3;
-  const int vbase = (4 * half + vj) * RS + 16 * (vg & 1) + 4 * vq;
+  const int vbase = (4 * half + vj) * RSV + 16 * (vg & 1) + 4 * vq;
 
   // ---- prologue: step 0 staged, step 1 in registers, ids of step 2 requested
   fetch_ids(kbeg);
@@ -161,7 +171,7 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
     for (int st = 0; st < 8; ++st)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = as_bf16x8(*(const u32x4 *)&Kb[(kb * 32 + q32) * RS + 16 * st + 8 * half]);
+        const bf16x8 kf = as_bf16x8(*(const u32x4 *)&Kb[(kb * 32 + q32) * RSK + 16 * st + 8 * half]);
         s[kb] = mfma32(kf, qf[st], s[kb]);
       }
 
@@ -213,9 +223,9 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const uint16_t *vp = Vb + vbase + (kb * 32 + s2 * 16) * RS + 32 * db;
+          const uint16_t *vp = Vb + vbase + (kb * 32 + s2 * 16) * RSV + 32 * db;
           const v4i16 lo = tr_read(vp);
-          const v4i16 hi = tr_read(vp + 8 * RS);
+          const v4i16 hi = tr_read(vp + 8 * RSV);
           const bf16x8 vf = __builtin_bit_cast(
               bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = mfma32(vf, pf[kb][s2], o[db]);
