@@ -151,12 +151,26 @@ std::vector<Item> xcd_order(const std::vector<Item> &items, const std::vector<in
   for (auto &p : pieces) {
     int best = (int)(std::min_element(load.begin(), load.end()) - load.begin());
     load[best] += p.work;
+    std::stable_sort(p.members.begin(), p.members.end(), [&](size_t a, size_t b) {
+      return item_work(items[a]) > item_work(items[b]);
+    });
     q[best].insert(q[best].end(), p.members.begin(), p.members.end());
   }
+  // Within a queue: longest first by coarse work bucket (eighths of the queue's
+  // longest item), and inside a bucket tiles sharing K/V together, so nearly
+  // equal tiles of one group run side by side and their K/V stays in the XCD's
+  // L2, while very unequal tiles still start longest first.
   size_t qlen = 0;
   for (auto &qq : q) {
-    std::stable_sort(qq.begin(), qq.end(),
-                     [&](size_t a, size_t b) { return item_work(items[a]) > item_work(items[b]); });
+    int64_t mx = 1;
+    for (size_t k : qq) mx = std::max(mx, item_work(items[k]));
+    auto bucket = [&](size_t k) { return item_work(items[k]) * 8 / (mx + 1); };
+    std::stable_sort(qq.begin(), qq.end(), [&](size_t a, size_t b) {
+      const int64_t ba = bucket(a), bb = bucket(b);
+      if (ba != bb) return ba > bb;
+      if (gkey[a] != gkey[b]) return gkey[a] < gkey[b];
+      return item_work(items[a]) > item_work(items[b]);
+    });
     qlen = std::max(qlen, qq.size());
   }
   Item pad{};
