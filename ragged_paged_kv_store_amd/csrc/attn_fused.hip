@@ -9,17 +9,17 @@
 
 namespace rpkv {
 
-template <bool BIGPAGE>
+template <int PM>
 __global__ __launch_bounds__(256, 2) void attn_fused_bf16_kernel(AttnArgs pre, AttnArgs dec,
                                                                  int32_t n_dec_blocks) {
   if ((int32_t)blockIdx.x < n_dec_blocks) {
-    if (BIGPAGE)
+    if (PM == 2)
       decode_chunk<dchunk::SlotsBig>(dec, blockIdx.x);
     else
       decode_chunk<dchunk::SlotsSmall>(dec, blockIdx.x);
     return;
   }
-  prefill_tile<BIGPAGE>(pre, blockIdx.x - n_dec_blocks);
+  prefill_tile<PM>(pre, blockIdx.x - n_dec_blocks);
 }
 
 int launch_fused_bf16(const AttnArgs &pre, const AttnArgs &dec, void *stream) {
@@ -29,12 +29,13 @@ int launch_fused_bf16(const AttnArgs &pre, const AttnArgs &dec, void *stream) {
   int32_t nd = (dec.n_items + kDecodeWavesPerBlock - 1) / kDecodeWavesPerBlock;
   nd = (nd + kNumXcd - 1) / kNumXcd * kNumXcd;
   const dim3 grid(nd + pre.n_items);
+  const dim3 block(256);
   if (pre.log2P >= 4)
-    hipLaunchKernelGGL(attn_fused_bf16_kernel<true>, grid, dim3(256), 0, (hipStream_t)stream, pre,
-                       dec, nd);
+    hipLaunchKernelGGL(attn_fused_bf16_kernel<2>, grid, block, 0, (hipStream_t)stream, pre, dec, nd);
+  else if (pre.log2P >= 2)
+    hipLaunchKernelGGL(attn_fused_bf16_kernel<1>, grid, block, 0, (hipStream_t)stream, pre, dec, nd);
   else
-    hipLaunchKernelGGL(attn_fused_bf16_kernel<false>, grid, dim3(256), 0, (hipStream_t)stream, pre,
-                       dec, nd);
+    hipLaunchKernelGGL(attn_fused_bf16_kernel<0>, grid, block, 0, (hipStream_t)stream, pre, dec, nd);
   return (int)hipGetLastError();
 }
 

@@ -5,12 +5,18 @@
 // so every K/V byte staged in LDS feeds G heads.  Each wavefront owns 32 rows.
 //
 // Per 64-key step:
-//  * the workgroup gathers 64 K rows and 64 V rows of its KV head through the
-//    page table (each thread 64 contiguous bytes of one row of each) one step
-//    ahead into registers, and stores both row-major in LDS (288-byte rows, two
-//    buffers).  When a page holds >= 16 keys the 16 rows a wavefront loads lie in
-//    one page, so the page id is a wave-uniform load and the row addresses are a
-//    scalar base plus a fixed lane offset;
+//  * K and V rows of the next step are gathered through the page table straight
+//    into LDS with gfx950's global-to-LDS loads (16 bytes per lane, each
+//    instruction filling 1 KiB = 4 rows), issued between the MFMAs of the
+//    current step: no registers, no LDS store instructions, and the address
+//    unit sees the loads spread over the step rather than in one burst.  K and
+//    V each have two buffers, so a step's loads have the whole step to land.
+//    Rows are 256 bytes, unpadded; the 16-byte chunks of row r are stored XOR
+//    (2*(r%8)) ^ ((r/8)%2), which keeps both the 16-byte K reads and the
+//    transposing V reads free of bank conflicts.  Keys past the range end load
+//    a row of zeros (V rows must be finite: their weights are zero).  When a
+//    page holds >= 16 keys, the 16 rows a wavefront loads lie in one page, so
+//    the page id is a wave-uniform load;
 //  * S^T = K Q^T with 32x32x16 MFMAs (A = K rows from LDS, B = the wavefront's Q
 //    rows held in registers): each lane then holds 32 logits of a single query
 //    row, so the row max and sum are in-lane plus one cross-half shuffle;
@@ -20,13 +26,13 @@
 //    range end; online softmax in base 2 with scale*log2(e) folded into one FMA;
 //    the O rescale is skipped unless the running max grows by more than 2^8;
 //  * O^T += V^T P^T with 32x32x16 MFMAs: the V^T operand comes from row-major V
-//    through gfx950's transposing LDS read (ds_read_b64_tr_b16: in each group of
-//    16 lanes, lane i receives element i%4 of the 8-byte chunks addressed by
-//    lanes 4j + i/4, j = 0..3), and P^T straight from the S^T accumulators; the
-//    key order the transposed reads produce matches the order the accumulators
-//    hold.
+//    through the transposing LDS read (ds_read_b64_tr_b16: in each group of 16
+//    lanes, lane i receives element i%4 of the 8-byte pieces addressed by lanes
+//    4j + i/4, j = 0..3), and P^T straight from the S^T accumulators; the key
+//    order the transposed reads produce matches the order the accumulators hold.
 // A tile writes its final output, or a partial (normalised fp32 O and base-2
-// log-sum-exp) when its key range is one of several (cascade prefix chunks).
+// log-sum-exp) when its key range is one of several (key splits of long
+// prefills, cascade prefix chunks).
 #pragma once
 
 #include "device_common.h"
@@ -36,35 +42,37 @@ namespace rpkv {
 namespace ptile {
 constexpr int D = 128;
 constexpr int BN = kPrefillKeys;  // 64 keys per step
-#ifndef VPAD
-#define VPAD 16
-#endif
-// LDS row strides (bf16).  K rows are read 16 lanes x 16 B per pass, one row
-// per lane: 272 B (68 dwords = 4 mod 64) puts 16 consecutive rows on distinct
-// banks.  V rows are read by the transposing read, 4 rows x 32 B per 16-lane
-// group, which wants the row stride apart by a multiple of 8 dwords.
-constexpr int RSK = D + 8;
-constexpr int RSV = D + VPAD;
+constexpr int ROWB = D * 2;       // bytes per K/V row in LDS
+constexpr int BUFB = BN * ROWB;   // bytes per K or V buffer
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-__device__ __forceinline__ v4i16 tr_read(const uint16_t *p) {
+// 16-byte chunk permutation of LDS row r (an involution on 0..15)
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ v4i16 tr_read(const unsigned char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_v4i16 *)(__attribute__((address_space(3))) void *)p);
 }
 }  // namespace ptile
 
-template <bool BIGPAGE>
+// source of the rows of keys past the range end
+static __device__ __attribute__((aligned(256))) uint32_t kZeroRow[ptile::ROWB / 4];
+
+// PM: page mode.  2: pages of >= 16 keys; 1 and 0: smaller pages.
+template <int PM>
 __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
   using namespace ptile;
-  // two K/V buffers: step t computes from buffer t%2 while step t+1 is staged
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * RSK];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * RSV];
+  constexpr bool BIGPAGE = PM == 2;
+  // four separate arrays, each addressed statically below, so the compiler can
+  // tell that loads into one buffer never alias reads of another
+  __shared__ __attribute__((aligned(1024))) unsigned char K0[BUFB], K1[BUFB];
+  __shared__ __attribute__((aligned(1024))) unsigned char V0[BUFB], V1[BUFB];
 
   const Item it = a.items[tile];
   if (it.ntok == 0) return;
-  // the wavefront index is uniform; saying so lets per-wave addresses (the page
-  // ids below) be scalar loads that do not wait on the vector-load counter
+  // the wavefront index is uniform; saying so keeps per-wave values (page ids,
+  // LDS destinations of the loads) in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int q32 = lane & 31, half = lane >> 5;
   const int G = a.G;
@@ -96,84 +104,126 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
   float mref = kNegInf, lrun = 0.f;
   const float c = a.scale_log2;
 
-  // ---- loader: row lr (wavefront w owns rows 16w..16w+15), 64-byte quarter part
+  // ---- loads: wavefront w fills rows 16w..16w+15 of a buffer with 4
+  // instructions of 4 rows; in instruction i lane l fills chunk l%16 of row
+  // 16w + 4i + l/16.
   const int32_t *ptrow = a.page_table + (int64_t)it.req * a.pt_stride;
   const int pmask = (1 << a.log2P) - 1;
-  const int lr = tid >> 2, part = tid & 3;
+  const int drow = lane >> 4, dpos = lane & 15;
   const char *kpool = (const char *)a.kpool;
   const char *vpool = (const char *)a.vpool;
+  const int64_t row_bytes = (int64_t)a.Hkv * (D * 2);
+  const int64_t head_off = (int64_t)it.kvh * (D * 2);
   const int kbeg = it.kbeg, kend = it.kend;
   const int nsteps = (kend - kbeg + BN - 1) / BN;
-  u32x4 kreg[4], vreg[4];
-  int32_t pg;  // page id for the next gather, -1 when none of the rows is valid
+  // page ids of the next loads, of an in-range key (the key is clamped to the
+  // range end): one per wavefront for big pages, else one per lane and row.
+  // They are plain vector loads, requested a step ahead and first read after
+  // the wait that ends that step, so reading them never waits on the
+  // outstanding K/V loads.
+  int32_t pg;
+  int32_t pgl[4];
 
+  auto page_of = [&](int key) { return ptrow[min(key, kend - 1) >> a.log2P]; };
   auto fetch_ids = [&](int kt) {
     if (BIGPAGE) {
-      const int k0 = kt + 16 * wave;
-      pg = __builtin_amdgcn_readfirstlane(k0 < kend ? ptrow[k0 >> a.log2P] : -1);
+      pg = page_of(kt + 16 * wave);
     } else {
-      const int key = kt + lr;
-      pg = key < kend ? ptrow[key >> a.log2P] : -1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pgl[i] = page_of(kt + 16 * wave + 4 * i + drow);
     }
   };
-  auto gather = [&](int kt) {
-    const int key = kt + lr;
-    if (pg >= 0 && key < kend) {
-      const int64_t slot = ((int64_t)clamp_page(pg, a.num_pages) << a.log2P) + (key & pmask);
-      const int64_t off = (slot * a.Hkv + it.kvh) * (D * 2) + part * 64;
+  // Source addresses of the 4 K and 4 V load instructions of one step: row
+  // 16*wave + 4i + drow, chunk ch_i = dpos ^ swz(4i + drow).  Steps start at
+  // multiples of 64 keys, so with pages of >= 16 keys the wavefront's 16 rows
+  // are the slots ((kt + 16w) % P) + 4i + drow of one page: a scalar base per
+  // step plus a per-lane offset fixed for the whole tile.
+  int32_t lane_off[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kreg[j] = *(const u32x4 *)(kpool + off + 16 * j);
+  for (int i = 0; i < 4; ++i)
+    lane_off[i] = (4 * i + drow) * (int32_t)row_bytes + (int32_t)head_off + 16 * (dpos ^ swz(4 * i + drow));
+  const int64_t page_bytes = row_bytes << a.log2P;
+  const char *ksrc[4], *vsrc[4];
+  auto step_sources = [&](int kt) {
+    if (BIGPAGE) {
+      const int32_t p = clamp_page(__builtin_amdgcn_readfirstlane(pg), a.num_pages);
+      const int64_t base = p * page_bytes + (int64_t)((kt + 16 * wave) & pmask) * row_bytes;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) vreg[j] = *(const u32x4 *)(vpool + off + 16 * j);
+      for (int i = 0; i < 4; ++i) {
+        ksrc[i] = kpool + base + lane_off[i];
+        vsrc[i] = vpool + base + lane_off[i];
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kreg[j] = u32x4{0u, 0u, 0u, 0u};
-        vreg[j] = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * i + drow;
+        const int64_t slot = ((int64_t)clamp_page(pgl[i], a.num_pages) << a.log2P) + ((kt + r) & pmask);
+        const int64_t off = slot * row_bytes + head_off + 16 * (dpos ^ swz(r));
+        ksrc[i] = kpool + off;
+        vsrc[i] = vpool + off;
+      }
+    }
+    if (kt + BN > kend) {  // the range ends in this step: rows past it read zeros
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool valid = kt + 16 * wave + 4 * i + drow < kend;
+        const char *z = (const char *)kZeroRow + 16 * (dpos ^ swz(4 * i + drow));
+        ksrc[i] = valid ? ksrc[i] : z;
+        vsrc[i] = valid ? vsrc[i] : z;
       }
     }
   };
-  auto stage = [&](int b) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4 *)&Ks[b][lr * RSK + part * 32 + 8 * j] = kreg[j];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4 *)&Vs[b][lr * RSV + part * 32 + 8 * j] = vreg[j];
+  auto load_rows = [&](const char *src, unsigned char *buf, int i) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)(buf + (16 * wave + 4 * i) * ROWB),
+                                     16, 0, 0);
   };
-  // transposed V read of this lane: in its 16-lane group g, lane 4j+q points at
-  // key row 4*half + j (+ 8*r) and channels 16*(g%2) + 4q (+ 32*db)
-  const int vg = lane >> 4, vj = (lane & 15) >> 2, vq = lane & 3;
-  const int vbase = (4 * half + vj) * RSV + 16 * (vg & 1) + 4 * vq;
 
-  // ---- prologue: step 0 staged, step 1 in registers, ids of step 2 requested
+  // K reads: lane (q32, half) reads row 32*kb + q32, logical chunk 2*st + half
+  const int kx = swz(q32);
+  // V transposed reads: in 16-lane group g, lane 4j+q reads row 4*half + j (+8)
+  // (+16*s2 + 32*kb), logical chunk 2*(g%2) + 4*db + q/2, bytes 8*(q%2)..
+  const int vg = lane >> 4, vj = (lane & 15) >> 2, vq = lane & 3;
+  const int vrow = 4 * half + vj;
+  const int vx = swz(vrow);  // row + 8 flips bit 0 of the permutation
+  const int vc0 = 2 * (vg & 1) + (vq >> 1);
+
+  // ---- prologue: step 0 loaded, ids of step 1 requested
   fetch_ids(kbeg);
-  gather(kbeg);
-  stage(0);
-  if (nsteps > 1) {
-    fetch_ids(kbeg + BN);
-    gather(kbeg + BN);
-  }
-  if (nsteps > 2) fetch_ids(kbeg + 2 * BN);
+  step_sources(kbeg);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_rows(ksrc[i], K0, i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_rows(vsrc[i], V0, i);
+  if (nsteps > 1) fetch_ids(kbeg + BN);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int t = 0; t < nsteps; ++t) {
+  // one step: compute from (Kb, Vb), load the next step into (Kn, Vn)
+  auto step = [&](int t, const unsigned char *Kb, const unsigned char *Vb, unsigned char *Kn,
+                  unsigned char *Vn) {
     const int kt = kbeg + t * BN;
-    const uint16_t *Kb = Ks[t & 1];
-    const uint16_t *Vb = Vs[t & 1];
+    // the last step loads rows past the range (zeros) into the idle buffers
+    step_sources(kt + BN);
 
     // ---- S^T = K Q^T: lane holds keys kt + 32*kb + (i/4)*8 + 4*half + i%4 of row m;
-    // two independent accumulation chains (key blocks 0 and 1) interleaved
+    // two accumulation chains (key blocks 0 and 1); the next step's loads go
+    // out between the MFMAs
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+    for (int st = 0; st < 8; ++st) {
+      const int ch = (2 * st + half) ^ kx;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = as_bf16x8(*(const u32x4 *)&Kb[(kb * 32 + q32) * RSK + 16 * st + 8 * half]);
+        const bf16x8 kf = as_bf16x8(*(const u32x4 *)(Kb + (kb * 32 + q32) * ROWB + 16 * ch));
         s[kb] = mfma32(kf, qf[st], s[kb]);
       }
+      if (st & 1) load_rows(ksrc[st >> 1], Kn, st >> 1);
+    }
 
     // ---- online softmax, base 2
     if ((kt + BN - 1 > amin) || (kt + BN > kend)) {
@@ -223,19 +273,25 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const uint16_t *vp = Vb + vbase + (kb * 32 + s2 * 16) * RSV + 32 * db;
-          const v4i16 lo = tr_read(vp);
-          const v4i16 hi = tr_read(vp + 8 * RSV);
+          const unsigned char *rp = Vb + (vrow + 16 * s2 + 32 * kb) * ROWB + 8 * (vq & 1);
+          const v4i16 lo = tr_read(rp + 16 * ((vc0 + 4 * db) ^ vx));
+          const v4i16 hi = tr_read(rp + 8 * ROWB + 16 * ((vc0 + 4 * db) ^ vx ^ 1));
           const bf16x8 vf = __builtin_bit_cast(
               bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = mfma32(vf, pf[kb][s2], o[db]);
+          if (db == 3) load_rows(vsrc[2 * kb + s2], Vn, 2 * kb + s2);
         }
 
-    // ---- pipeline: stage step t+1, gather step t+2, request ids of step t+3
-    if (t + 1 < nsteps) stage((t + 1) & 1);
-    if (t + 2 < nsteps) gather(kt + 2 * BN);
-    if (t + 3 < nsteps) fetch_ids(kt + 3 * BN);
+    // ---- page ids for the loads of the step after next (the loads above used
+    // the current ones); then the next step's rows have landed (this
+    // wavefront's), then all waves
+    if (t + 2 < nsteps) fetch_ids(kt + 2 * BN);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  for (int t = 0; t < nsteps; t += 2) {
+    step(t, K0, V0, K1, V1);
+    if (t + 1 < nsteps) step(t + 1, K1, V1, K0, V0);
   }
 
   // ---- epilogue: this lane holds channels 32*db + (i/4)*8 + 4*half + i%4 of row m
