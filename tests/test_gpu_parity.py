@@ -1,6 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle on the same
 seeded inputs.  Bars: KV-pool store bit-exact; outputs within max-abs 2e-2
 (bf16) / 1e-4 (fp32) of the oracle."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -91,7 +93,7 @@ EDGE = [
 def test_edge_cases(case):
     name, dtype, Hq, Hkv, P, n, L = case
     D = 128
-    rng = np.random.default_rng(abs(hash(name)) % 2 ** 32)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
     spec = synth.build(name, dtype, Hq, Hkv, D, P, n, L, 7, rng, 1.3)
     check_full(spec)
 
