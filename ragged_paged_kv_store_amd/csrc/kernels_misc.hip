@@ -19,11 +19,12 @@ __global__ __launch_bounds__(256) void store_kv_kernel(const u32x4 *__restrict__
   if (i >= total) return;
   const int64_t t = i / chunks_per_row;
   const int32_t c = (int32_t)(i - t * chunks_per_row);
+  // the row loads do not wait for the slot: one memory round trip, then stores
   const int32_t s = slots[t];
-  if (s < 0 || s >= num_slots) return;
-  const int64_t dst = (int64_t)s * chunks_per_row + c;
   const u32x4 kk = k[i];
   const u32x4 vv = v[i];
+  if (s < 0 || s >= num_slots) return;
+  const int64_t dst = (int64_t)s * chunks_per_row + c;
   kpool[dst] = kk;
   vpool[dst] = vv;
 }
@@ -57,12 +58,48 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t *__restrict__ 
                                                     void *__restrict__ out, int32_t Hq,
                                                     int32_t dtype) {
   constexpr int PER = D / 64;
+  constexpr int kFast = 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.y * 4 + wave;
   if (h >= Hq) return;
   const int32_t tok = merge[blockIdx.x * 3 + 0];
   const int32_t pb = merge[blockIdx.x * 3 + 1];
   const int32_t ns = merge[blockIdx.x * 3 + 2];
+  const int64_t ob = ((int64_t)tok * Hq + h) * D + lane * PER;
+  if (ns <= kFast) {
+    // the usual case: every log-sum-exp and partial row is requested at once
+    // (one memory round trip after the merge record), then combined
+    const float *op = o_part + ((int64_t)pb * Hq + h) * D + lane * PER;
+    const int64_t stride = (int64_t)Hq * D;
+    const float lv = lane < ns ? lse_part[(int64_t)(pb + lane) * Hq + h] : kNegInf;
+    float v[kFast][PER];
+#pragma unroll
+    for (int u = 0; u < kFast; ++u)
+#pragma unroll
+      for (int j = 0; j < PER; ++j) v[u][j] = u < ns ? op[u * stride + j] : 0.f;
+    float M = lv;
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
+    const float wl = M == kNegInf ? 0.f : fast_exp2(lv - M);  // 2^-inf = 0
+    float W = 0.f, acc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int u = 0; u < kFast; ++u) {
+      const float w = __shfl(wl, u, 64);
+      W += w;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) acc[j] += w * v[u][j];
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    if (dtype == RPKV_F32) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) ((float *)out)[ob + j] = acc[j] * inv;
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) ((uint16_t *)out)[ob + j] = f32_to_bf16(acc[j] * inv);
+    }
+    return;
+  }
   float M = kNegInf;
   for (int s0 = 0; s0 < ns; s0 += 64)
     if (s0 + lane < ns) M = fmaxf(M, lse_part[(int64_t)(pb + s0 + lane) * Hq + h]);
@@ -102,7 +139,6 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t *__restrict__ 
     for (int off = 32; off > 0; off >>= 1) W += shfl_xor(W, off);
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
-  const int64_t ob = ((int64_t)tok * Hq + h) * D + lane * PER;
   if (dtype == RPKV_F32) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) ((float *)out)[ob + j] = acc[j] * inv;
