@@ -214,15 +214,31 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
+    // K fragments read two 16-channel slices ahead of the MFMAs that use them
+    bf16x8 kf[3][2];
+    auto kread = [&](int st, bf16x8(&dst)[2]) {
       const int ch = (2 * st + half) ^ kx;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = as_bf16x8(*(const u32x4 *)(Kb + (kb * 32 + q32) * ROWB + 16 * ch));
-        s[kb] = mfma32(kf, qf[st], s[kb]);
-      }
+      for (int kb = 0; kb < 2; ++kb)
+        dst[kb] = as_bf16x8(*(const u32x4 *)(Kb + (kb * 32 + q32) * ROWB + 16 * ch));
+    };
+    kread(0, kf[0]);
+    kread(1, kf[1]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      if (st + 2 < 8) kread(st + 2, kf[(st + 2) % 3]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kf[st % 3][kb], qf[st], s[kb]);
       if (st & 1) load_rows(ksrc[st >> 1], Kn, st >> 1);
+    }
+    // keep that order: reads two slices ahead of their MFMAs, the next step's
+    // K loads between them (0x100: LDS reads, 0x8: MFMA, 0x20: memory reads)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (st + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (st & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
 
     // ---- online softmax, base 2
@@ -281,6 +297,15 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
           o[db] = mfma32(vf, pf[kb][s2], o[db]);
           if (db == 3) load_rows(vsrc[2 * kb + s2], Vn, 2 * kb + s2);
         }
+    // transposing reads one 16-key block ahead of its 4 MFMAs, a V load after
+    // each block (0x100: LDS reads, 0x8: MFMA, 0x20: memory reads)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+      if (blk + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+    }
 
     // ---- page ids for the loads of the step after next (the loads above used
     // the current ones); then the next step's rows have landed (this
