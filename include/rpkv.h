@@ -260,6 +260,38 @@ rpkv_status rpkv_forward(rpkv_plan *plan, const void *q, const void *k, const vo
                          const int32_t *slot_mapping, void *k_pool, void *v_pool, void *out,
                          float scale, void *stream);
 
+/* ------------------------------------------------- device-side metadata */
+
+/* Packed-batch metadata built on the device ("Variable-length batching and one
+ * mixed forward pass": the batch builder of its worked example, and the
+ * source-code notes on building positions, query_start_loc, slot_mapping and
+ * logits_indices without a host loop).  From per-request, device-resident
+ *   num_computed[i]  tokens of request i already in the cache (>= 0)
+ *   n[i]             new tokens of request i this step (>= 0)
+ *   need_logits[i]   nonzero if request i samples (NULL: every request)
+ * it writes
+ *   query_start_loc[B+1]  running sum of n (query_start_loc[0] = 0)
+ *   seq_lens[B]           num_computed + n
+ *   positions[t]          num_computed[i] + r for the r-th new token t of request i
+ *   slot_mapping[t]       table[i][p / P] * P + p % P with p = positions[t]
+ *                         (-1 if p / P >= bt_cols)
+ *   logits_indices[m]     query_start_loc[i+1] - 1 for the m-th request (in order)
+ *                         with need_logits
+ *   counts[0]             N = sum of n;  counts[1] = number of logits indices.
+ * All arrays are int32 device memory owned by the caller: positions and
+ * slot_mapping hold max_tokens entries (tokens at or past max_tokens are not
+ * written: check counts[0] <= max_tokens), logits_indices holds B entries.
+ * block_tables is [B, bt_stride] with bt_cols valid columns per row.  Two kernels
+ * on `stream`; no host synchronisation and no allocation, so the call can be
+ * captured in a HIP graph and replayed with new inputs.  Arguments are checked
+ * on the host; a failed check enqueues nothing. */
+rpkv_status rpkv_build_metadata(int32_t batch, const int32_t *num_computed, const int32_t *n,
+                                const uint8_t *need_logits, const int32_t *block_tables,
+                                int64_t bt_stride, int32_t bt_cols, int32_t page_size,
+                                int64_t max_tokens, int32_t *query_start_loc, int32_t *seq_lens,
+                                int32_t *positions, int32_t *slot_mapping,
+                                int32_t *logits_indices, int32_t *counts, void *stream);
+
 /* ------------------------------------------------------- instrumentation */
 
 /* Enable (1) or disable (0) per-launch HIP-event timing on this plan, with room

@@ -33,6 +33,7 @@ EXPORTS = (
     "rpkv_plan_destroy", "rpkv_plan_batch", "rpkv_prepare_metadata", "rpkv_workspace_bytes",
     "rpkv_last_indices", "rpkv_plan_get_info", "rpkv_plan_get_items", "rpkv_plan_get_token_list",
     "rpkv_store_kv", "rpkv_attend", "rpkv_forward", "rpkv_timing_enable", "rpkv_timing_collect",
+    "rpkv_build_metadata",
 )
 
 
@@ -98,6 +99,7 @@ def _load():
         "rpkv_forward": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp]),
         "rpkv_timing_enable": (i32, [vp, i32, i32]),
         "rpkv_timing_collect": (i32, [vp, P(KernelTimes)]),
+        "rpkv_build_metadata": (i32, [i32, vp, vp, vp, vp, i64, i32, i32, i64] + [vp] * 7),
     }
     for name, (res, args) in sigs.items():
         f = getattr(L, name)
@@ -130,6 +132,46 @@ def _stream(stream) -> Optional[int]:
         import torch
         return torch.cuda.current_stream().cuda_stream
     return getattr(stream, "cuda_stream", stream)
+
+
+def build_metadata(num_computed, n, block_tables, page_size: int, need_logits=None,
+                   max_tokens: Optional[int] = None, out=None, stream=None):
+    """rpkv_build_metadata on device tensors (int32 num_computed [B], n [B],
+    block_tables [B, stride]; uint8 need_logits [B] or None).  Returns a dict of
+    int32 device tensors: query_start_loc [B+1], seq_lens [B], positions and
+    slot_mapping [max_tokens], logits_indices [B], counts [2] (N, number of
+    logits indices).  `out` may pass preallocated tensors of those names (for
+    graph capture); nothing is synchronised."""
+    import torch
+    B = int(num_computed.shape[0])
+    for name, t in (("num_computed", num_computed), ("n", n), ("block_tables", block_tables)):
+        if not t.is_cuda or t.dtype != torch.int32 or t.shape[0] != B:
+            raise ValueError(f"{name}: int32 device tensor with {B} rows expected")
+    if block_tables.dim() != 2 or block_tables.stride(1) != 1:
+        raise ValueError("block_tables: 2-D with unit column stride expected")
+    if need_logits is not None and (need_logits.dtype != torch.uint8 or need_logits.shape[0] != B
+                                    or not need_logits.is_cuda):
+        raise ValueError("need_logits: uint8 device tensor [B] expected")
+    if max_tokens is None:
+        max_tokens = int(n.sum().item())
+    dev = num_computed.device
+    o = dict(out or {})
+    shapes = {"query_start_loc": B + 1, "seq_lens": B, "positions": max_tokens,
+              "slot_mapping": max_tokens, "logits_indices": max(B, 1), "counts": 2}
+    for k, sz in shapes.items():
+        if k not in o:
+            o[k] = torch.empty(max(sz, 1), dtype=torch.int32, device=dev)
+        elif o[k].dtype != torch.int32 or o[k].numel() < sz or not o[k].is_contiguous():
+            raise ValueError(f"out[{k}]: contiguous int32 with >= {sz} entries expected")
+    st = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    _check(lib.rpkv_build_metadata(B, num_computed.data_ptr(), n.data_ptr(),
+                                   None if need_logits is None else need_logits.data_ptr(),
+                                   block_tables.data_ptr(), block_tables.stride(0),
+                                   block_tables.shape[1], page_size, max_tokens,
+                                   o["query_start_loc"].data_ptr(), o["seq_lens"].data_ptr(),
+                                   o["positions"].data_ptr(), o["slot_mapping"].data_ptr(),
+                                   o["logits_indices"].data_ptr(), o["counts"].data_ptr(), st))
+    return o
 
 
 def supports(**kw) -> Tuple[bool, str]:

@@ -417,6 +417,34 @@ rpkv_status rpkv_forward(rpkv_plan *p, const void *q, const void *k, const void 
   return rpkv_attend(p, q, kpool, vpool, out, scale, stream);
 }
 
+rpkv_status rpkv_build_metadata(int32_t batch, const int32_t *num_computed, const int32_t *n,
+                                const uint8_t *need_logits, const int32_t *block_tables,
+                                int64_t bt_stride, int32_t bt_cols, int32_t page_size,
+                                int64_t max_tokens, int32_t *query_start_loc, int32_t *seq_lens,
+                                int32_t *positions, int32_t *slot_mapping,
+                                int32_t *logits_indices, int32_t *counts, void *stream) {
+  if (batch < 0) return fail(RPKV_ERR_INVALID_ARG, "batch < 0");
+  if (max_tokens < 0) return fail(RPKV_ERR_INVALID_ARG, "max_tokens < 0");
+  if (page_size < 1 || page_size > 1024 || (page_size & (page_size - 1)))
+    return fail(RPKV_ERR_INVALID_ARG, "page_size must be a power of two in [1, 1024]");
+  if (bt_cols < 0 || bt_stride < bt_cols)
+    return fail(RPKV_ERR_INVALID_ARG, "block table: need 0 <= cols <= stride");
+  if (!query_start_loc || !seq_lens || !logits_indices || !counts)
+    return fail(RPKV_ERR_INVALID_ARG, "query_start_loc, seq_lens, logits_indices, counts must be non-NULL");
+  if (batch > 0 && (!num_computed || !n || !block_tables))
+    return fail(RPKV_ERR_INVALID_ARG, "num_computed, n and block_tables must be non-NULL");
+  if (max_tokens > 0 && (!positions || !slot_mapping))
+    return fail(RPKV_ERR_INVALID_ARG, "positions and slot_mapping must be non-NULL");
+  int log2P = 0;
+  while ((1 << log2P) < page_size) ++log2P;
+  const int e = rpkv::launch_build_metadata(batch, num_computed, n, need_logits, block_tables,
+                                            bt_stride, bt_cols, log2P, max_tokens, query_start_loc,
+                                            seq_lens, positions, slot_mapping, logits_indices,
+                                            counts, stream);
+  if (e) return hip_fail(e, "build_metadata launch");
+  return RPKV_OK;
+}
+
 rpkv_status rpkv_timing_enable(rpkv_plan *p, int32_t enable, int32_t max_launches) {
   if (!p) return fail(RPKV_ERR_INVALID_ARG, "plan is NULL");
   if (enable && max_launches <= 0) return fail(RPKV_ERR_INVALID_ARG, "max_launches must be > 0");

@@ -99,6 +99,10 @@ int launch_decode_bf16(const AttnArgs &a, void *stream);
 // split-KV chunks and MFMA tiles in one grid (chunks first)
 int launch_fused_bf16(const AttnArgs &pre, const AttnArgs &dec, void *stream);
 int launch_attn_f32(const AttnArgs &a, void *stream);
+int launch_build_metadata(int32_t B, const int32_t *nc, const int32_t *n, const uint8_t *need,
+                          const int32_t *tables, int64_t stride, int32_t cols, int32_t log2P,
+                          int64_t max_tokens, int32_t *qsl, int32_t *seq, int32_t *positions,
+                          int32_t *slots, int32_t *lg, int32_t *counts, void *stream);
 int launch_merge(const int32_t *merge, int32_t n_merge, const float *o_part,
                  const float *lse_part, void *out, int32_t Hq, int32_t D, int32_t dtype,
                  void *stream);

@@ -69,6 +69,22 @@ def make_plan(rp, spec, **kw):
                    max_tokens=max(spec.T, 1), max_pages_per_req=spec.page_table.shape[1], **kw)
 
 
+@pytest.mark.parametrize("batch,P,stride,cols,null", [
+    (-1, 16, 8, 8, None), (2, 12, 8, 8, None), (2, 16, 4, 8, None), (2, 16, 8, -1, None),
+    (2, 16, 8, 8, "n"), (2, 16, 8, 8, "counts"),
+])
+def test_build_metadata_rejects_bad_arguments(rp, batch, P, stride, cols, null):
+    """Checked on the host before anything is enqueued (no GPU needed)."""
+    fake = ctypes.c_void_p(0x1000)
+    args = {k: fake for k in ("nc", "n", "bt", "qsl", "seq", "pos", "slots", "lg", "counts")}
+    if null:
+        args[null] = None
+    st = rp.lib.rpkv_build_metadata(batch, args["nc"], args["n"], None, args["bt"], stride, cols, P,
+                                    16, args["qsl"], args["seq"], args["pos"], args["slots"],
+                                    args["lg"], args["counts"], None)
+    assert st == 1, rp.lib.rpkv_last_error()
+
+
 def test_last_indices_worked_example(rp):
     g = _golden.load("p1_worked_example.txt")
     p = rp.Plan(num_q_heads=16, num_kv_heads=8, head_dim=128, page_size=1, dtype=0, max_batch=3,
