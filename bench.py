@@ -115,6 +115,38 @@ def measured_traffic(workload: str, kernel: str):
     return k["bytes_per_launch"]
 
 
+def metadata_build_us(spec, db, rp, torch, reps: int = 50):
+    """The batch's positions / query_start_loc / seq_lens / slot_mapping /
+    logits_indices: built on the device (rpkv_build_metadata, HIP events around
+    `reps` calls on the current stream) and, for comparison, vectorised with
+    numpy on the host (an engine's usual build)."""
+    nc = (spec.L - spec.n).astype(np.int32)
+    n = spec.n.astype(np.int32)
+    nc_d = torch.from_numpy(nc).cuda()
+    n_d = torch.from_numpy(n).cuda()
+    out = rp.build_metadata(nc_d, n_d, db.page_table, spec.P, max_tokens=max(spec.T, 1))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        rp.build_metadata(nc_d, n_d, db.page_table, spec.P, max_tokens=max(spec.T, 1), out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    dev_us = e0.elapsed_time(e1) * 1e3 / reps
+    pt = spec.page_table
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        qsl = np.concatenate(([0], np.cumsum(n))).astype(np.int32)
+        req = np.repeat(np.arange(spec.bs), n)
+        pos = (nc[req] + np.arange(int(qsl[-1])) - qsl[:-1][req]).astype(np.int32)
+        slots = pt[req, pos // spec.P] * spec.P + pos % spec.P
+        seq = nc + n
+        logits = qsl[1:] - 1
+    host_us = (time.perf_counter() - t0) * 1e6 / reps
+    del slots, seq, logits
+    return {"device": round(dev_us, 2), "host_numpy": round(host_us, 2)}
+
+
 def cpu_baseline(spec, db, H, budget_flops: float = 40e9):
     """The fp64 oracle as it stands, on the host, over one layer of the batch:
     every row when the layer is within ~40 GFLOP (about 30 core-seconds),
@@ -172,6 +204,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=LAYERS,
                     help="layers per step (a model has 32; fewer only for short profiling runs)")
+    ap.add_argument("--graph", action="store_true",
+                    help="uniform decode batches only: capture the whole step (device metadata "
+                         "build + 32 graph-decode forwards) in one HIP graph and time its replays")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -230,6 +265,78 @@ def main():
             q, k, v = qkv[l % nq]
             plan.forward(q, k, v, sm, kp, vp, outs[l % nq], spec.scale, stream=stream)
 
+    if args.graph:
+        n0 = int(spec.n[0])
+        if not (np.all(spec.n == n0) and n0 * spec.G <= 16 and spec.dtype == "bf16"):
+            print("bench.py: --graph needs a uniform bf16 decode batch (e.g. --workload c3)",
+                  file=sys.stderr)
+            sys.exit(2)
+        gplan = H.make_plan(spec)
+        max_seq = int(spec.L.max())
+        gplan.graph_decode_init(spec.bs, n0, max_seq)
+        nc_d = torch.from_numpy((spec.L - spec.n).astype(np.int32)).cuda()
+        n_d = torch.from_numpy(spec.n.astype(np.int32)).cuda()
+        meta = {k: torch.empty(sz, dtype=torch.int32, device="cuda") for k, sz in
+                (("query_start_loc", spec.bs + 1), ("seq_lens", spec.bs), ("positions", spec.T),
+                 ("slot_mapping", spec.T), ("logits_indices", spec.bs), ("counts", 2))}
+        gstream = torch.cuda.Stream()
+
+        def gstep(st):
+            rp.build_metadata(nc_d, n_d, pt, spec.P, max_tokens=spec.T, out=meta, stream=st)
+            for l in range(layers):
+                kp, vp = pools[l % npools]
+                q, k, v = qkv[l % nq]
+                gplan.graph_decode_forward(spec.bs, q, k, v, meta["slot_mapping"], kp, vp,
+                                           meta["seq_lens"], pt, outs[l % nq], spec.scale,
+                                           stream=st)
+
+        with torch.cuda.stream(gstream):
+            gstep(gstream.cuda_stream)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gstream):
+            gstep(torch.cuda.current_stream().cuda_stream)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        # per-kernel durations of the same launches, eagerly, with HIP events
+        gplan.timing_enable(True, max_launches=4 * layers * args.steps + 64)
+        for _ in range(args.steps):
+            gstep(stream.cuda_stream)
+        gtimes = gplan.timing_collect()
+        gplan.timing_enable(False)
+        torch.cuda.synchronize()
+        alg = algorithmic(spec, 0)
+        dec_n, dec_ms = gtimes["decode"]
+        kv_rate = alg["kv_total"] * layers / (graph_ms * 1e-3) / 1e9
+        avg_s = dec_ms / dec_n * 1e-3
+        line = {
+            "metric": "attention TFLOP/s (prefill-heavy) and KV-read GB/s (decode-heavy), 1 MI355X",
+            "value": round(kv_rate, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(graph_ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
+            "data": "synthetic (seeded N(0,1) tensors, seeded page allocation)",
+            "config": {"workload": desc, "layers_per_step": layers, "pool_sets": npools,
+                       "batch": spec.bs, "tokens": spec.T,
+                       "step": f"one HIP graph: device metadata build + {layers} x graph-decode "
+                               "forward (store_kv + split-KV + merge)"},
+            "roofline": {"bound": "hbm", "achieved": alg["kv_decode"] / avg_s / 1e9,
+                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": alg["kv_decode"] / avg_s / 1e9 / PEAK_HBM_GBPS,
+                         "kernel": "graph decode", "traffic": None},
+            "cpu_baseline": None,
+            "extra": {"per_kernel": {k: {"launches": nn, "avg_us": (ms * 1e3 / nn) if nn else None}
+                                     for k, (nn, ms) in gtimes.items()},
+                      "layer_us": round(graph_ms * 1e3 / layers, 2)},
+        }
+        print(json.dumps(line), flush=True)
+        return
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -281,6 +388,7 @@ def main():
     roof["kernel"] = dom
     roof["traffic"] = measured_traffic(args.workload, dom) if layers == LAYERS else None
 
+    meta_us = metadata_build_us(spec, layer0, rp, torch)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(spec, layer0, H)
@@ -317,6 +425,7 @@ def main():
             "split_kv_in_fused_launch": bool(times.get("fused", (0, 0))[0]),
             "algorithmic_per_layer": alg,
             "plan": info,
+            "metadata_build_us": meta_us,
         },
     }
     print(json.dumps(line), flush=True)

@@ -260,6 +260,41 @@ rpkv_status rpkv_forward(rpkv_plan *plan, const void *q, const void *k, const vo
                          const int32_t *slot_mapping, void *k_pool, void *v_pool, void *out,
                          float scale, void *stream);
 
+/* ---------------------------------------------- graph-capturable decode */
+
+/* Pure-decode steps for HIP-graph capture and replay (the pages' capture
+ * interface: mini-sglang "The attention backend and a reference
+ * implementation", the capture methods of the backend interface; vLLM
+ * "Attention backends", Step 6, support for uniform decode batches).  A uniform
+ * batch: request i has q_len new tokens, rows i*q_len .. of q/k/v/out, and a
+ * KV length L_i (including them) read from a device array at run time, so one
+ * captured sequence of launches replays for any lengths: update seq_lens, the
+ * page table, slot_mapping and q/k/v in place (rpkv_build_metadata can write
+ * seq_lens and slot_mapping on the device), then replay.
+ *
+ * rpkv_graph_decode_init: fixes the capacities (max_batch requests, q_len new
+ * tokens each, lengths up to max_seq_len), picks one key chunk (>= 256 keys, at
+ * most 8 chunks per request) and allocates the plan-owned partial workspace.
+ * Call it outside capture.  bf16 only; q_len * Hq / Hkv <= 16. */
+rpkv_status rpkv_graph_decode_init(rpkv_plan *plan, int32_t max_batch, int32_t q_len,
+                                   int32_t max_seq_len);
+
+/* rpkv_graph_decode_forward: store_kv of the batch*q_len tokens, then attention
+ * of each request's rows over its L_i keys (bottom-right causal mask, split-KV
+ * chunks merged by log-sum-exp), on `stream`.  No host synchronisation, no
+ * allocation, grids fixed by `batch`: capturable.
+ *   seq_lens    device int32 [batch]: q_len <= L_i <= max_seq_len (a request with
+ *               L_i < q_len is skipped; keys past max_seq_len are ignored)
+ *   page_table  device int32 [batch, pt_stride], pt_cols >= ceil(max_seq_len / P)
+ *               valid columns
+ *   q, out      device [batch*q_len, Hq, D]; k, v [batch*q_len, Hkv, D];
+ *   slot_mapping device int32 [batch*q_len] (as for rpkv_store_kv). */
+rpkv_status rpkv_graph_decode_forward(rpkv_plan *plan, int32_t batch, const void *q, const void *k,
+                                      const void *v, const int32_t *slot_mapping, void *k_pool,
+                                      void *v_pool, const int32_t *seq_lens,
+                                      const int32_t *page_table, int64_t pt_stride,
+                                      int32_t pt_cols, void *out, float scale, void *stream);
+
 /* ------------------------------------------------- device-side metadata */
 
 /* Packed-batch metadata built on the device ("Variable-length batching and one

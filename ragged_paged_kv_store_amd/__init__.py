@@ -33,7 +33,7 @@ EXPORTS = (
     "rpkv_plan_destroy", "rpkv_plan_batch", "rpkv_prepare_metadata", "rpkv_workspace_bytes",
     "rpkv_last_indices", "rpkv_plan_get_info", "rpkv_plan_get_items", "rpkv_plan_get_token_list",
     "rpkv_store_kv", "rpkv_attend", "rpkv_forward", "rpkv_timing_enable", "rpkv_timing_collect",
-    "rpkv_build_metadata",
+    "rpkv_build_metadata", "rpkv_graph_decode_init", "rpkv_graph_decode_forward",
 )
 
 
@@ -100,6 +100,9 @@ def _load():
         "rpkv_timing_enable": (i32, [vp, i32, i32]),
         "rpkv_timing_collect": (i32, [vp, P(KernelTimes)]),
         "rpkv_build_metadata": (i32, [i32, vp, vp, vp, vp, i64, i32, i32, i64] + [vp] * 7),
+        "rpkv_graph_decode_init": (i32, [vp, i32, i32, i32]),
+        "rpkv_graph_decode_forward": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp,
+                                            ctypes.c_float, vp]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(L, name)
@@ -371,6 +374,37 @@ class Plan:
         _check(lib.rpkv_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(slot_mapping),
                                 _ptr(k_pool), _ptr(v_pool), _ptr(out), float(scale),
                                 _stream(stream)))
+
+    # ---------------------------------------------- graph-capturable decode
+    def graph_decode_init(self, max_batch: int, q_len: int, max_seq_len: int):
+        _check(lib.rpkv_graph_decode_init(self._h, max_batch, q_len, max_seq_len))
+        self._graph = (max_batch, q_len, max_seq_len)
+
+    def graph_decode_forward(self, batch: int, q, k, v, slot_mapping, k_pool, v_pool, seq_lens,
+                             page_table, out, scale: float, stream=None):
+        """Capturable: every check here is on shapes only (no device reads)."""
+        import torch
+        if getattr(self, "_graph", None) is None:
+            raise RpkvError(4, "graph_decode_init first")
+        _, q_len, _ = self._graph
+        T = batch * q_len
+        self._check_slots(slot_mapping, T)
+        self._check_rows("q", q, self.shape.num_q_heads, T)
+        self._check_rows("out", out, self.shape.num_q_heads, T)
+        self._check_rows("k", k, self.shape.num_kv_heads, T)
+        self._check_rows("v", v, self.shape.num_kv_heads, T)
+        self._check_pool("k_pool", k_pool)
+        self._check_pool("v_pool", v_pool)
+        if (not seq_lens.is_cuda or seq_lens.dtype != torch.int32 or seq_lens.numel() < batch
+                or not seq_lens.is_contiguous()):
+            raise ValueError("seq_lens: contiguous int32 device tensor with >= batch entries")
+        if (not page_table.is_cuda or page_table.dtype != torch.int32 or page_table.dim() != 2
+                or page_table.shape[0] < batch or page_table.stride(1) != 1):
+            raise ValueError("page_table: int32 device tensor [>= batch, cols], unit column stride")
+        _check(lib.rpkv_graph_decode_forward(
+            self._h, batch, _ptr(q), _ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(k_pool),
+            _ptr(v_pool), seq_lens.data_ptr(), page_table.data_ptr(), page_table.stride(0),
+            page_table.shape[1], _ptr(out), float(scale), _stream(stream)))
 
     # ------------------------------------------------------- instrumentation
     def timing_enable(self, enable: bool, max_launches: int = 4096):

@@ -57,6 +57,11 @@ struct rpkv_plan {
   std::vector<hipEvent_t> ev;
   std::vector<int32_t> ev_kind;
   int32_t n_rec = 0;
+  // graph-capturable decode: fixed capacities and plan-owned partials
+  int32_t g_max_batch = 0, g_q_len = 0, g_chunk = 0, g_maxc = 0, g_max_seq = 0;
+  float *g_opart = nullptr;
+  float *g_lse = nullptr;
+  int g_device = -1;
 };
 
 namespace {
@@ -127,11 +132,13 @@ rpkv_status rpkv_plan_create(const rpkv_shape *shape, rpkv_plan **out) {
 
 void rpkv_plan_destroy(rpkv_plan *p) {
   if (!p) return;
-  if (p->dmeta || p->hmeta[0] || p->hmeta[1] || !p->ev.empty()) {
+  if (p->dmeta || p->hmeta[0] || p->hmeta[1] || !p->ev.empty() || p->g_opart) {
     if (p->device >= 0) (void)hipSetDevice(p->device);
+    else if (p->g_device >= 0) (void)hipSetDevice(p->g_device);
     (void)hipDeviceSynchronize();
   }
   if (p->dmeta) (void)hipFree(p->dmeta);
+  if (p->g_opart) (void)hipFree(p->g_opart);
   for (int i = 0; i < 2; ++i) {
     if (p->hmeta[i]) (void)hipHostFree(p->hmeta[i]);
     if (p->hev[i]) (void)hipEventDestroy(p->hev[i]);
@@ -415,6 +422,107 @@ rpkv_status rpkv_forward(rpkv_plan *p, const void *q, const void *k, const void 
   rpkv_status st = rpkv_store_kv(p, k, v, slots, p->hp.T, kpool, vpool, stream);
   if (st != RPKV_OK) return st;
   return rpkv_attend(p, q, kpool, vpool, out, scale, stream);
+}
+
+rpkv_status rpkv_graph_decode_init(rpkv_plan *p, int32_t max_batch, int32_t q_len,
+                                   int32_t max_seq_len) {
+  if (!p) return fail(RPKV_ERR_INVALID_ARG, "plan is NULL");
+  if (p->s.dtype != RPKV_BF16) return fail(RPKV_ERR_UNSUPPORTED, "graph decode is bf16 only");
+  if (max_batch < 1 || q_len < 1 || max_seq_len < q_len)
+    return fail(RPKV_ERR_INVALID_ARG, "need max_batch >= 1, q_len >= 1, max_seq_len >= q_len");
+  if ((int64_t)q_len * p->s.G() > rpkv::kDecodeRows)
+    return fail(RPKV_ERR_UNSUPPORTED, "q_len * Hq / Hkv must be <= 16 (one split-KV item)");
+  if ((int64_t)max_seq_len > (int64_t)p->s.max_pages_per_req * p->s.P)
+    return fail(RPKV_ERR_CAPACITY, "max_seq_len exceeds max_pages_per_req * page_size");
+  if ((int64_t)max_batch * q_len > INT32_MAX / 8)
+    return fail(RPKV_ERR_INVALID_ARG, "max_batch * q_len too large");
+  // at most 8 chunks per request (the merge's one-round-trip path), >= 256 keys
+  const int32_t chunk = std::max<int32_t>(256, (int32_t)(((max_seq_len + 7) / 8 + 63) / 64 * 64));
+  const int32_t maxc = (max_seq_len + chunk - 1) / chunk;
+  int dev = 0;
+  int e = hipGetDevice(&dev);
+  if (e) return hip_fail(e, "hipGetDevice");
+  const size_t rows = (size_t)max_batch * q_len * maxc * p->s.Hq;
+  const size_t obytes = align256(rows * p->s.D * sizeof(float));
+  const size_t bytes = obytes + align256(rows * sizeof(float));
+  if (p->g_opart) {
+    e = hipDeviceSynchronize();
+    if (e) return hip_fail(e, "hipDeviceSynchronize");
+    (void)hipFree(p->g_opart);
+    p->g_opart = p->g_lse = nullptr;
+    p->g_max_batch = 0;
+  }
+  void *buf = nullptr;
+  e = hipMalloc(&buf, bytes);
+  if (e) return hip_fail(e, "hipMalloc (graph decode partials)");
+  p->g_opart = (float *)buf;
+  p->g_lse = (float *)((char *)buf + obytes);
+  p->g_max_batch = max_batch;
+  p->g_q_len = q_len;
+  p->g_chunk = chunk;
+  p->g_maxc = maxc;
+  p->g_max_seq = max_seq_len;
+  p->g_device = dev;
+  return RPKV_OK;
+}
+
+rpkv_status rpkv_graph_decode_forward(rpkv_plan *p, int32_t batch, const void *q, const void *k,
+                                      const void *v, const int32_t *slot_mapping, void *kpool,
+                                      void *vpool, const int32_t *seq_lens,
+                                      const int32_t *page_table, int64_t pt_stride,
+                                      int32_t pt_cols, void *out, float scale, void *stream) {
+  if (!p) return fail(RPKV_ERR_INVALID_ARG, "plan is NULL");
+  if (!p->g_opart) return fail(RPKV_ERR_NOT_PREPARED, "graph decode not initialised");
+  if (batch < 0 || batch > p->g_max_batch)
+    return fail(RPKV_ERR_CAPACITY, "batch exceeds the graph decode capacity");
+  if (batch == 0) return RPKV_OK;
+  if (!q || !k || !v || !slot_mapping || !kpool || !vpool || !seq_lens || !page_table || !out)
+    return fail(RPKV_ERR_INVALID_ARG, "q, k, v, slot_mapping, pools, seq_lens, page_table, out must be non-NULL");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)kpool | (uintptr_t)vpool |
+       (uintptr_t)out) & 15)
+    return fail(RPKV_ERR_INVALID_ARG, "q, k, v, pools and out must be 16-byte aligned");
+  if (pt_cols < 0 || pt_stride < pt_cols ||
+      (int64_t)pt_cols * p->s.P < (int64_t)p->g_max_seq)
+    return fail(RPKV_ERR_INVALID_ARG, "page table must have ceil(max_seq_len / page_size) columns");
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(RPKV_ERR_INVALID_ARG, "scale must be finite and positive");
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev != p->g_device)
+    return fail(RPKV_ERR_INVALID_ARG, "graph decode on a device other than its init's");
+  const int32_t T = batch * p->g_q_len;
+  const int64_t row_bytes = (int64_t)p->s.Hkv * p->s.D * 2;
+  const int64_t num_slots = p->s.num_pages * p->s.P;
+  rpkv_status st = timed(p, RPKV_KERNEL_STORE, stream, [&] {
+    return rpkv::launch_store_kv(k, v, slot_mapping, T, row_bytes, num_slots, kpool, vpool, stream);
+  }, "store_kv launch");
+  if (st != RPKV_OK) return st;
+  rpkv::AttnArgs a{};
+  a.q = q;
+  a.kpool = kpool;
+  a.vpool = vpool;
+  a.out = out;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.tok_pbase = nullptr;
+  a.pstride = p->g_maxc;
+  a.o_part = p->g_opart;
+  a.lse_part = p->g_lse;
+  a.Hq = p->s.Hq;
+  a.Hkv = p->s.Hkv;
+  a.G = p->s.G();
+  a.D = p->s.D;
+  a.log2P = p->s.log2P;
+  a.num_pages = p->s.num_pages;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  st = timed(p, RPKV_KERNEL_DECODE, stream, [&] {
+    return rpkv::launch_graph_decode_bf16(a, seq_lens, p->g_q_len, p->g_chunk, p->g_maxc, batch,
+                                          stream);
+  }, "graph decode launch");
+  if (st != RPKV_OK || p->g_maxc <= 1) return st;
+  return timed(p, RPKV_KERNEL_MERGE, stream, [&] {
+    return rpkv::launch_graph_merge(seq_lens, p->g_q_len, p->g_chunk, p->g_maxc, T, p->g_opart,
+                                    p->g_lse, out, p->s.Hq, p->s.D, p->s.dtype, stream);
+  }, "graph merge launch");
 }
 
 rpkv_status rpkv_build_metadata(int32_t batch, const int32_t *num_computed, const int32_t *n,

@@ -191,17 +191,12 @@ __device__ __forceinline__ void step(State &st, Regs &r, const bf16x8 (&qf)[4], 
 
 }  // namespace dchunk
 
-// One wavefront of a 4-wavefront block runs item block*4 + wave.
+// One wavefront runs one item.  A partial result of token t goes to partial
+// row tok_pbase[t] + split, or t * pstride + split when tok_pbase is NULL.
 template <class Slots>
-__device__ __forceinline__ void decode_chunk(const AttnArgs &a, int block) {
+__device__ __forceinline__ void decode_item(const AttnArgs &a, const Item &it) {
   using namespace dchunk;
-  // uniform wavefront index: the item and its page ids are then scalar loads,
-  // which do not wait on the vector-load counter of the K/V loads in flight
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int ii = block * kDecodeWavesPerBlock + wave;
-  if (ii >= a.n_items) return;
-  const Item it = a.items[ii];
-  if (it.ntok == 0) return;
+  const int lane = threadIdx.x & 63;
   const int G = a.G;
   const int col = lane & 15, grp = lane >> 4;
   const int rows = it.ntok * G;
@@ -268,7 +263,7 @@ __device__ __forceinline__ void decode_chunk(const AttnArgs &a, int block) {
       *(u32x4 *)(orow + 8 * (4 * grp + i)) = w;
     }
   } else {
-    const int64_t pi = (int64_t)a.tok_pbase[tok] + it.split;
+    const int64_t pi = (a.tok_pbase ? (int64_t)a.tok_pbase[tok] : (int64_t)tok * a.pstride) + it.split;
     float *prow = a.o_part + (pi * a.Hq + qh) * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -283,6 +278,19 @@ __device__ __forceinline__ void decode_chunk(const AttnArgs &a, int block) {
     }
     if (grp == 0) a.lse_part[pi * a.Hq + qh] = l > 0.f ? st.m + fast_log2(l) : kNegInf;
   }
+}
+
+// One wavefront of a 4-wavefront block runs item block*4 + wave of the list.
+template <class Slots>
+__device__ __forceinline__ void decode_chunk(const AttnArgs &a, int block) {
+  // uniform wavefront index: the item and its page ids are then scalar loads,
+  // which do not wait on the vector-load counter of the K/V loads in flight
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ii = block * kDecodeWavesPerBlock + wave;
+  if (ii >= a.n_items) return;
+  const Item it = a.items[ii];
+  if (it.ntok == 0) return;
+  decode_item<Slots>(a, it);
 }
 
 }  // namespace rpkv

@@ -52,19 +52,15 @@ int launch_store_kv(const void *k, const void *v, const int32_t *slots, int64_t 
 // lane s holds partial s's weight (64 partials per pass), each lane D/64
 // channels; the partial rows are independent loads issued back to back.
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(const int32_t *__restrict__ merge,
-                                                    const float *__restrict__ o_part,
-                                                    const float *__restrict__ lse_part,
-                                                    void *__restrict__ out, int32_t Hq,
-                                                    int32_t dtype) {
+__device__ __forceinline__ void merge_one(int32_t tok, int32_t pb, int32_t ns,
+                                          const float *__restrict__ o_part,
+                                          const float *__restrict__ lse_part,
+                                          void *__restrict__ out, int32_t Hq, int32_t dtype) {
   constexpr int PER = D / 64;
   constexpr int kFast = 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.y * 4 + wave;
   if (h >= Hq) return;
-  const int32_t tok = merge[blockIdx.x * 3 + 0];
-  const int32_t pb = merge[blockIdx.x * 3 + 1];
-  const int32_t ns = merge[blockIdx.x * 3 + 2];
   const int64_t ob = ((int64_t)tok * Hq + h) * D + lane * PER;
   if (ns <= kFast) {
     // the usual case: every log-sum-exp and partial row is requested at once
@@ -146,6 +142,47 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t *__restrict__ 
 #pragma unroll
     for (int j = 0; j < PER; ++j) ((uint16_t *)out)[ob + j] = f32_to_bf16(acc[j] * inv);
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const int32_t *__restrict__ merge,
+                                                    const float *__restrict__ o_part,
+                                                    const float *__restrict__ lse_part,
+                                                    void *__restrict__ out, int32_t Hq,
+                                                    int32_t dtype) {
+  merge_one<D>(merge[blockIdx.x * 3 + 0], merge[blockIdx.x * 3 + 1], merge[blockIdx.x * 3 + 2],
+               o_part, lse_part, out, Hq, dtype);
+}
+
+// The graph-decode merge: token t of a uniform batch has min(ceil(L_i / chunk),
+// maxc) partials at rows t * maxc + c (none to merge when there is one: the
+// chunk wrote the output).
+template <int D>
+__global__ __launch_bounds__(256) void graph_merge_kernel(const int32_t *__restrict__ seq_lens,
+                                                          int32_t q_len, int32_t chunk, int32_t maxc,
+                                                          const float *__restrict__ o_part,
+                                                          const float *__restrict__ lse_part,
+                                                          void *__restrict__ out, int32_t Hq,
+                                                          int32_t dtype) {
+  const int32_t tok = blockIdx.x;
+  const int32_t L = seq_lens[tok / q_len];
+  const int32_t ns = min((L + chunk - 1) / chunk, maxc);
+  if (ns <= 1 || L < q_len) return;
+  merge_one<D>(tok, tok * maxc, ns, o_part, lse_part, out, Hq, dtype);
+}
+
+int launch_graph_merge(const int32_t *seq_lens, int32_t q_len, int32_t chunk, int32_t maxc,
+                       int32_t T, const float *o_part, const float *lse_part, void *out,
+                       int32_t Hq, int32_t D, int32_t dtype, void *stream) {
+  if (T <= 0) return 0;
+  const dim3 grid(T, (Hq + 3) / 4);
+  if (D == 128)
+    hipLaunchKernelGGL(graph_merge_kernel<128>, grid, dim3(256), 0, (hipStream_t)stream, seq_lens,
+                       q_len, chunk, maxc, o_part, lse_part, out, Hq, dtype);
+  else
+    hipLaunchKernelGGL(graph_merge_kernel<64>, grid, dim3(256), 0, (hipStream_t)stream, seq_lens,
+                       q_len, chunk, maxc, o_part, lse_part, out, Hq, dtype);
+  return (int)hipGetLastError();
 }
 
 int launch_merge(const int32_t *merge, int32_t n_merge, const float *o_part,

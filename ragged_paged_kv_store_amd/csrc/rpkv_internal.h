@@ -89,6 +89,7 @@ struct AttnArgs {
   int32_t Hq, Hkv, G, D, log2P;
   int64_t num_pages;
   float scale_log2;   // scale * log2(e)
+  int32_t pstride;    // partials per token when tok_pbase is NULL (graph decode)
 };
 
 int launch_store_kv(const void *k, const void *v, const int32_t *slots, int64_t T,
@@ -99,6 +100,11 @@ int launch_decode_bf16(const AttnArgs &a, void *stream);
 // split-KV chunks and MFMA tiles in one grid (chunks first)
 int launch_fused_bf16(const AttnArgs &pre, const AttnArgs &dec, void *stream);
 int launch_attn_f32(const AttnArgs &a, void *stream);
+int launch_graph_decode_bf16(const AttnArgs &a, const int32_t *seq_lens, int32_t q_len,
+                             int32_t chunk, int32_t maxc, int32_t batch, void *stream);
+int launch_graph_merge(const int32_t *seq_lens, int32_t q_len, int32_t chunk, int32_t maxc,
+                       int32_t T, const float *o_part, const float *lse_part, void *out,
+                       int32_t Hq, int32_t D, int32_t dtype, void *stream);
 int launch_build_metadata(int32_t B, const int32_t *nc, const int32_t *n, const uint8_t *need,
                           const int32_t *tables, int64_t stride, int32_t cols, int32_t log2P,
                           int64_t max_tokens, int32_t *qsl, int32_t *seq, int32_t *positions,
