@@ -207,6 +207,40 @@ rpkv_status rpkv_prepare_metadata(rpkv_plan *plan, int32_t batch, const int32_t 
                                   const rpkv_prefix_group *groups_host, int32_t num_groups,
                                   void *workspace_dev, size_t workspace_bytes, void *stream);
 
+/* prepare_metadata with the page table in FlashInfer's CSR form ("SGLang source
+ * walkthrough: Attention backends", 3.2 Page Table): request i's pages are
+ * page_indices[page_indptr[i] .. page_indptr[i+1]) and its last page holds
+ * last_page_len[i] tokens, so L_i = (pages_i - 1) * page_size + last_page_len[i]
+ * (0 for a request without pages).  The lengths are derived on the host; the
+ * rows are expanded into a plan-owned dense table on `stream` after the
+ * metadata upload (attend/forward must follow on the same stream).
+ *   page_indptr_host    [batch+1] host, page_indptr[0] = 0, non-decreasing,
+ *                       pages_i <= max_pages_per_req
+ *   last_page_len_host  [batch] host, in [1, page_size] for requests with pages
+ *   page_indices_dev    device int32 [page_indptr[batch]]
+ *   page_indices_host   optional host copy (page ids then checked, cascade hints
+ *                       checked), else NULL
+ * Other arguments and errors as rpkv_prepare_metadata. */
+rpkv_status rpkv_prepare_metadata_csr(rpkv_plan *plan, int32_t batch,
+                                      const int32_t *cu_seqlens_q_host,
+                                      const int32_t *page_indptr_host,
+                                      const int32_t *last_page_len_host,
+                                      const int32_t *page_indices_dev,
+                                      const int32_t *page_indices_host,
+                                      const rpkv_prefix_group *groups_host, int32_t num_groups,
+                                      void *workspace_dev, size_t workspace_bytes, void *stream);
+
+/* Rewrite a block table whose blocks hold `factor` kernel pages each into a
+ * table of kernel pages (vLLM "Attention backends", Step 5: the attention group
+ * rewrites the block table when the kernel's blocks are smaller than the cache
+ * manager's): out[i][j*factor + r] = table[i][j] * factor + r for j < cols,
+ * r < factor.  Device int32 arrays owned by the caller, one kernel on `stream`.
+ *   table [batch, stride] with cols valid columns; out [batch, out_stride],
+ *   out_stride >= cols * factor. */
+rpkv_status rpkv_rewrite_block_table(int32_t batch, const int32_t *table, int64_t stride,
+                                     int32_t cols, int32_t factor, int32_t *out,
+                                     int64_t out_stride, void *stream);
+
 /* Device workspace bytes the last planned batch needs (0 if none). */
 rpkv_status rpkv_workspace_bytes(const rpkv_plan *plan, size_t *bytes);
 

@@ -34,6 +34,7 @@ EXPORTS = (
     "rpkv_last_indices", "rpkv_plan_get_info", "rpkv_plan_get_items", "rpkv_plan_get_token_list",
     "rpkv_store_kv", "rpkv_attend", "rpkv_forward", "rpkv_timing_enable", "rpkv_timing_collect",
     "rpkv_build_metadata", "rpkv_graph_decode_init", "rpkv_graph_decode_forward",
+    "rpkv_prepare_metadata_csr", "rpkv_rewrite_block_table",
 )
 
 
@@ -101,6 +102,8 @@ def _load():
         "rpkv_timing_collect": (i32, [vp, P(KernelTimes)]),
         "rpkv_build_metadata": (i32, [i32, vp, vp, vp, vp, i64, i32, i32, i64] + [vp] * 7),
         "rpkv_graph_decode_init": (i32, [vp, i32, i32, i32]),
+        "rpkv_prepare_metadata_csr": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]),
+        "rpkv_rewrite_block_table": (i32, [i32, vp, i64, i32, i32, vp, i64, vp]),
         "rpkv_graph_decode_forward": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp,
                                             ctypes.c_float, vp]),
     }
@@ -175,6 +178,20 @@ def build_metadata(num_computed, n, block_tables, page_size: int, need_logits=No
                                    o["positions"].data_ptr(), o["slot_mapping"].data_ptr(),
                                    o["logits_indices"].data_ptr(), o["counts"].data_ptr(), st))
     return o
+
+
+def rewrite_block_table(table, factor: int, stream=None):
+    """rpkv_rewrite_block_table: a [B, cols] int32 device table of blocks of
+    `factor` kernel pages -> a new [B, cols*factor] table of kernel pages."""
+    import torch
+    if not (table.is_cuda and table.dtype == torch.int32 and table.dim() == 2 and
+            table.stride(1) == 1):
+        raise ValueError("table must be a 2-D int32 CUDA tensor with unit column stride")
+    B, cols = table.shape
+    out = torch.empty((B, cols * factor), dtype=torch.int32, device=table.device)
+    _check(lib.rpkv_rewrite_block_table(B, table.data_ptr(), table.stride(0), cols, factor,
+                                        out.data_ptr(), out.stride(0), _stream(stream)))
+    return out
 
 
 def supports(**kw) -> Tuple[bool, str]:
@@ -307,6 +324,43 @@ class Plan:
             _check(st)
             break
         self._pt = page_table
+        self.batch = bs
+        self.num_tokens = int(cu[-1]) if len(cu) else 0
+
+    def prepare_csr(self, cu_q, page_indptr, last_page_len, page_indices, page_indices_host=None,
+                    groups: Sequence[Tuple[int, int, int]] = (), stream=None):
+        """prepare_metadata_csr: the page table as FlashInfer's (page_indices [K]
+        int32 device tensor, page_indptr [B+1] and last_page_len [B] on the host)."""
+        import torch
+        cu = _i32(cu_q)
+        ip = _i32(page_indptr)
+        lp = _i32(last_page_len)
+        bs = len(lp)
+        if not (page_indices.is_cuda and page_indices.dtype == torch.int32 and
+                page_indices.is_contiguous()):
+            raise ValueError("page_indices must be a contiguous int32 CUDA tensor")
+        if len(ip) != bs + 1 or (bs and page_indices.numel() < int(ip[-1])):
+            raise ValueError("page_indptr must have batch+1 entries within page_indices")
+        pih = None if page_indices_host is None else _i32(page_indices_host)
+        garr = (PrefixGroup * max(len(groups), 1))(*[PrefixGroup(*g) for g in groups])
+        gptr = ctypes.cast(garr, ctypes.c_void_p) if groups else None
+        s = _stream(stream)
+        for _ in range(2):
+            ws = self.workspace
+            st = lib.rpkv_prepare_metadata_csr(
+                self._h, bs, cu.ctypes.data, ip.ctypes.data, lp.ctypes.data,
+                page_indices.data_ptr(), None if pih is None else pih.ctypes.data, gptr,
+                len(groups), None if ws is None else ws.data_ptr(),
+                0 if ws is None else ws.numel(), s)
+            if st == 3:
+                need = ctypes.c_size_t()
+                _check(lib.rpkv_workspace_bytes(self._h, ctypes.byref(need)))
+                self.workspace = torch.empty(int(need.value * 1.25) + 256, dtype=torch.uint8,
+                                             device=page_indices.device)
+                continue
+            _check(st)
+            break
+        self._pt = page_indices
         self.batch = bs
         self.num_tokens = int(cu[-1]) if len(cu) else 0
 

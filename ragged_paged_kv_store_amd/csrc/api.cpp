@@ -38,7 +38,10 @@ struct rpkv_plan {
   // device copy of the work partition
   char *dmeta = nullptr;
   size_t dmeta_cap = 0;
-  size_t off_pre = 0, off_dec = 0, off_pbase = 0, off_merge = 0, off_tok = 0, meta_bytes = 0;
+  size_t off_pre = 0, off_dec = 0, off_pbase = 0, off_merge = 0, off_tok = 0, off_indptr = 0,
+         meta_bytes = 0;
+  // dense copy of a CSR page table (plan-owned, [max_batch, max_pages_per_req])
+  int32_t *csr_table = nullptr;
   // pinned staging, two buffers so a new batch never overwrites one in flight
   char *hmeta[2] = {nullptr, nullptr};
   size_t hmeta_cap[2] = {0, 0};
@@ -138,6 +141,7 @@ void rpkv_plan_destroy(rpkv_plan *p) {
     (void)hipDeviceSynchronize();
   }
   if (p->dmeta) (void)hipFree(p->dmeta);
+  if (p->csr_table) (void)hipFree(p->csr_table);
   if (p->g_opart) (void)hipFree(p->g_opart);
   for (int i = 0; i < 2; ++i) {
     if (p->hmeta[i]) (void)hipHostFree(p->hmeta[i]);
@@ -167,15 +171,23 @@ rpkv_status rpkv_plan_batch(rpkv_plan *p, int32_t batch, const int32_t *cu, cons
   return RPKV_OK;
 }
 
-rpkv_status rpkv_prepare_metadata(rpkv_plan *p, int32_t batch, const int32_t *cu,
-                                  const int32_t *seqlens, const int32_t *pt_dev, int64_t pt_stride,
-                                  int32_t cols, const int32_t *pt_host,
-                                  const rpkv_prefix_group *groups, int32_t ngroups, void *ws,
-                                  size_t ws_bytes, void *stream) {
+namespace {
+
+// prepare_metadata; csr_indptr (a CSR page table's row offsets) rides along in
+// the metadata upload
+rpkv_status prepare_impl(rpkv_plan *p, int32_t batch, const int32_t *cu, const int32_t *seqlens,
+                         const int32_t *pt_dev, int64_t pt_stride, int32_t cols,
+                         const int32_t *pt_host, const rpkv_prefix_group *groups, int32_t ngroups,
+                         void *ws, size_t ws_bytes, void *stream,
+                         const std::vector<int32_t> *csr_indptr) {
   if (!p) return fail(RPKV_ERR_INVALID_ARG, "plan is NULL");
   if (pt_stride < cols) return fail(RPKV_ERR_INVALID_ARG, "page_table_stride < page_table_cols");
   rpkv_status st = rpkv_plan_batch(p, batch, cu, seqlens, cols, pt_host, groups, ngroups);
   if (st != RPKV_OK) return st;
+  if (csr_indptr)
+    p->hp.csr_indptr = *csr_indptr;
+  else
+    p->hp.csr_indptr.clear();
   p->planned = false;  // becomes usable only once uploaded
   const HostPlan &hp = p->hp;
   bool any_keys = false;
@@ -206,6 +218,8 @@ rpkv_status rpkv_prepare_metadata(rpkv_plan *p, int32_t batch, const int32_t *cu
   off = align256(off + hp.merge.size() * sizeof(int32_t));
   p->off_tok = off;
   off = align256(off + hp.toklist.size() * sizeof(int32_t));
+  p->off_indptr = off;
+  off = align256(off + hp.csr_indptr.size() * sizeof(int32_t));
   const size_t bytes = std::max<size_t>(off, 256);
 
   if (bytes > p->dmeta_cap) {
@@ -250,6 +264,8 @@ rpkv_status rpkv_prepare_metadata(rpkv_plan *p, int32_t batch, const int32_t *cu
   if (!hp.merge.empty()) std::memcpy(h + p->off_merge, hp.merge.data(), hp.merge.size() * sizeof(int32_t));
   if (!hp.toklist.empty())
     std::memcpy(h + p->off_tok, hp.toklist.data(), hp.toklist.size() * sizeof(int32_t));
+  if (!hp.csr_indptr.empty())
+    std::memcpy(h + p->off_indptr, hp.csr_indptr.data(), hp.csr_indptr.size() * sizeof(int32_t));
   e = hipMemcpyAsync(p->dmeta, h, bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
   if (e) return hip_fail(e, "hipMemcpyAsync (metadata)");
   e = hipEventRecord(p->hev[c], (hipStream_t)stream);
@@ -269,6 +285,86 @@ rpkv_status rpkv_prepare_metadata(rpkv_plan *p, int32_t batch, const int32_t *cu
   }
   p->planned = true;
   p->prepared = true;
+  return RPKV_OK;
+}
+
+}  // namespace
+
+rpkv_status rpkv_prepare_metadata(rpkv_plan *p, int32_t batch, const int32_t *cu,
+                                  const int32_t *seqlens, const int32_t *pt_dev, int64_t pt_stride,
+                                  int32_t cols, const int32_t *pt_host,
+                                  const rpkv_prefix_group *groups, int32_t ngroups, void *ws,
+                                  size_t ws_bytes, void *stream) {
+  return prepare_impl(p, batch, cu, seqlens, pt_dev, pt_stride, cols, pt_host, groups, ngroups, ws,
+                      ws_bytes, stream, nullptr);
+}
+
+rpkv_status rpkv_prepare_metadata_csr(rpkv_plan *p, int32_t batch, const int32_t *cu,
+                                      const int32_t *indptr, const int32_t *last_page_len,
+                                      const int32_t *indices_dev, const int32_t *indices_host,
+                                      const rpkv_prefix_group *groups, int32_t ngroups, void *ws,
+                                      size_t ws_bytes, void *stream) {
+  if (!p) return fail(RPKV_ERR_INVALID_ARG, "plan is NULL");
+  if (batch < 0) return fail(RPKV_ERR_INVALID_ARG, "batch < 0");
+  if (batch > p->s.max_batch) return fail(RPKV_ERR_CAPACITY, "batch exceeds max_batch");
+  if (batch > 0 && (!indptr || !last_page_len || !cu))
+    return fail(RPKV_ERR_INVALID_ARG, "cu_seqlens_q, page_indptr and last_page_len must be non-NULL");
+  if (batch > 0 && indptr[0] != 0) return fail(RPKV_ERR_INVALID_ARG, "page_indptr[0] must be 0");
+  const int32_t P = p->s.P;
+  std::vector<int32_t> L(batch), iptr(batch > 0 ? indptr : nullptr, batch > 0 ? indptr + batch + 1 : nullptr);
+  int32_t cols = 1;
+  for (int32_t i = 0; i < batch; ++i) {
+    const int32_t pages = indptr[i + 1] - indptr[i];
+    if (pages < 0) return fail(RPKV_ERR_INVALID_ARG, "page_indptr must be non-decreasing");
+    if (pages > p->s.max_pages_per_req)
+      return fail(RPKV_ERR_CAPACITY, "a request has more pages than max_pages_per_req");
+    if (pages > 0 && (last_page_len[i] < 1 || last_page_len[i] > P))
+      return fail(RPKV_ERR_INVALID_ARG, "last_page_len must be in [1, page_size]");
+    L[i] = pages > 0 ? (pages - 1) * P + last_page_len[i] : 0;
+    cols = std::max(cols, pages);
+  }
+  const int32_t total = batch > 0 ? indptr[batch] : 0;
+  if (total > 0 && !indices_dev) return fail(RPKV_ERR_INVALID_ARG, "page_indices_dev is NULL");
+  std::vector<int32_t> host;
+  if (indices_host) {
+    host.assign((size_t)batch * cols, 0);
+    for (int32_t i = 0; i < batch; ++i)
+      std::memcpy(host.data() + (size_t)i * cols, indices_host + indptr[i],
+                  (size_t)(indptr[i + 1] - indptr[i]) * sizeof(int32_t));
+  }
+  if (!p->csr_table) {
+    int e = hipMalloc((void **)&p->csr_table,
+                      std::max<size_t>(1, (size_t)p->s.max_batch * p->s.max_pages_per_req) * sizeof(int32_t));
+    if (e) {
+      p->csr_table = nullptr;
+      return hip_fail(e, "hipMalloc (dense copy of the CSR page table)");
+    }
+  }
+  rpkv_status st = prepare_impl(p, batch, cu, L.data(), p->csr_table, p->s.max_pages_per_req, cols,
+                                indices_host ? host.data() : nullptr, groups, ngroups, ws, ws_bytes,
+                                stream, &iptr);
+  if (st != RPKV_OK) return st;
+  // expand the rows on the stream, after the upload of the offsets
+  const int e = rpkv::launch_csr_to_dense(batch, (const int32_t *)(p->dmeta + p->off_indptr),
+                                          indices_dev, p->csr_table, p->s.max_pages_per_req, stream);
+  if (e) {
+    p->prepared = false;
+    return hip_fail(e, "csr_to_dense launch");
+  }
+  return RPKV_OK;
+}
+
+rpkv_status rpkv_rewrite_block_table(int32_t batch, const int32_t *table, int64_t stride,
+                                     int32_t cols, int32_t factor, int32_t *out,
+                                     int64_t out_stride, void *stream) {
+  if (batch < 0 || cols < 0 || factor < 1)
+    return fail(RPKV_ERR_INVALID_ARG, "need batch >= 0, cols >= 0, factor >= 1");
+  if (stride < cols || out_stride < (int64_t)cols * factor || (int64_t)cols * factor > INT32_MAX)
+    return fail(RPKV_ERR_INVALID_ARG, "need stride >= cols and out_stride >= cols * factor");
+  if (batch > 0 && cols > 0 && (!table || !out))
+    return fail(RPKV_ERR_INVALID_ARG, "table and out must be non-NULL");
+  const int e = rpkv::launch_rewrite_blocks(batch, table, stride, cols, factor, out, out_stride, stream);
+  if (e) return hip_fail(e, "rewrite_block_table launch");
   return RPKV_OK;
 }
 

@@ -97,4 +97,48 @@ int launch_build_metadata(int32_t B, const int32_t *nc, const int32_t *n, const 
   return (int)hipGetLastError();
 }
 
+// FlashInfer-style page table to the dense table the kernels read: row i gets
+// the page ids page_indices[indptr[i] .. indptr[i+1]) ("SGLang source
+// walkthrough, Attention backends", section 3.2).
+__global__ __launch_bounds__(256) void csr_to_dense_kernel(const int32_t *__restrict__ indptr,
+                                                           const int32_t *__restrict__ indices,
+                                                           int32_t *__restrict__ dense,
+                                                           int64_t stride) {
+  const int i = blockIdx.x;
+  const int a = indptr[i], b = indptr[i + 1];
+  int32_t *row = dense + (int64_t)i * stride;
+  for (int j = a + (int)threadIdx.x; j < b; j += blockDim.x) row[j - a] = indices[j];
+}
+
+// A block table for blocks of `factor` kernel pages each, rewritten into kernel
+// pages: out[i][j*factor + r] = table[i][j]*factor + r (vLLM "Attention backends":
+// the attention group's rewrite into kernel blocks).
+__global__ __launch_bounds__(256) void rewrite_blocks_kernel(const int32_t *__restrict__ table,
+                                                             int64_t stride, int32_t cols,
+                                                             int32_t factor,
+                                                             int32_t *__restrict__ out,
+                                                             int64_t out_stride) {
+  const int i = blockIdx.x;
+  const int32_t *row = table + (int64_t)i * stride;
+  int32_t *orow = out + (int64_t)i * out_stride;
+  const int n = cols * factor;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) orow[j] = row[j / factor] * factor + j % factor;
+}
+
+int launch_csr_to_dense(int32_t B, const int32_t *indptr, const int32_t *indices, int32_t *dense,
+                        int64_t stride, void *stream) {
+  if (B <= 0) return 0;
+  hipLaunchKernelGGL(csr_to_dense_kernel, dim3(B), dim3(256), 0, (hipStream_t)stream, indptr,
+                     indices, dense, stride);
+  return (int)hipGetLastError();
+}
+
+int launch_rewrite_blocks(int32_t B, const int32_t *table, int64_t stride, int32_t cols,
+                          int32_t factor, int32_t *out, int64_t out_stride, void *stream) {
+  if (B <= 0 || cols <= 0) return 0;
+  hipLaunchKernelGGL(rewrite_blocks_kernel, dim3(B), dim3(256), 0, (hipStream_t)stream, table,
+                     stride, cols, factor, out, out_stride);
+  return (int)hipGetLastError();
+}
+
 }  // namespace rpkv

@@ -45,6 +45,7 @@ constexpr int kConcurrentKeysPerStep = 24;
 struct HostPlan {
   int32_t batch = 0, T = 0, max_q = 0, max_k = 0;
   std::vector<int32_t> cu_q, L;
+  std::vector<int32_t> csr_indptr;  // [batch+1] when the page table came in CSR form
   std::vector<Item> prefill;   // XCD-interleaved, padded to a multiple of 8
   std::vector<Item> decode;    // longest first
   std::vector<int32_t> tok_pbase;  // [T] partial base or -1
@@ -105,6 +106,10 @@ int launch_graph_decode_bf16(const AttnArgs &a, const int32_t *seq_lens, int32_t
 int launch_graph_merge(const int32_t *seq_lens, int32_t q_len, int32_t chunk, int32_t maxc,
                        int32_t T, const float *o_part, const float *lse_part, void *out,
                        int32_t Hq, int32_t D, int32_t dtype, void *stream);
+int launch_csr_to_dense(int32_t B, const int32_t *indptr, const int32_t *indices, int32_t *dense,
+                        int64_t stride, void *stream);
+int launch_rewrite_blocks(int32_t B, const int32_t *table, int64_t stride, int32_t cols,
+                          int32_t factor, int32_t *out, int64_t out_stride, void *stream);
 int launch_build_metadata(int32_t B, const int32_t *nc, const int32_t *n, const uint8_t *need,
                           const int32_t *tables, int64_t stride, int32_t cols, int32_t log2P,
                           int64_t max_tokens, int32_t *qsl, int32_t *seq, int32_t *positions,
