@@ -56,3 +56,53 @@ def test_pins_fail_on_planted_mistake(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutation {name}:\n{r.stdout[-2000:]}"
+
+
+# ---------------------------------------------------------------- prefix tree
+TREE_SRC = os.path.join(ROOT, "oracle", "prefix_tree.py")
+TREE_MUTATIONS = {
+    "offer_rounds_up": ("return (int(L) - int(n)) // int(P)",
+                        "return -(-(int(L) - int(n)) // int(P))"),
+    "offer_counts_new_tokens": ("return (int(L) - int(n)) // int(P)", "return int(L) // int(P)"),
+    "shallowest_depth": ("depth_of[s] = max(depth_of.get(s, 0), k)",
+                         "depth_of[s] = depth_of.get(s, k)"),
+    "singleton_nodes": ("if len(members) >= 2:", "if len(members) >= 1:"),
+    "prune_from_root": ("base = 0 if a is None else depth_of[a] * P", "base = 0"),
+    "largest_parent": ("(best is None or len(t) < len(best))",
+                       "(best is None or len(t) > len(best))"),
+    "ineligible_join": ("E = [j for j in range(bs) if eligible[j]]", "E = list(range(bs))"),
+}
+
+_TREE_RUNNER = """
+import importlib.util, sys
+spec = importlib.util.spec_from_file_location("oracle.prefix_tree", sys.argv[1])
+mod = importlib.util.module_from_spec(spec)
+sys.modules["oracle.prefix_tree"] = mod
+spec.loader.exec_module(mod)
+import oracle
+oracle.prefix_tree = mod
+import pytest
+sys.exit(pytest.main(["-x", "-q", "-p", "no:cacheprovider", sys.argv[2]]))
+"""
+
+
+@pytest.mark.parametrize("name", sorted(TREE_MUTATIONS))
+def test_tree_pins_fail_on_planted_mistake(name, tmp_path):
+    orig, repl = TREE_MUTATIONS[name]
+    src = open(TREE_SRC).read()
+    assert src.count(orig) == 1, f"mutation anchor not unique/present: {name}"
+    mod = tmp_path / "prefix_tree_mut.py"
+    mod.write_text(src.replace(orig, repl))
+    r = subprocess.run([sys.executable, "-c", _TREE_RUNNER, str(mod),
+                        os.path.join(ROOT, "tests", "test_oracle_prefix_tree.py")],
+                       cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutation {name}:\n{r.stdout[-2000:]}"
+
+
+def test_tree_runner_passes_unmodified(tmp_path):
+    mod = tmp_path / "prefix_tree_copy.py"
+    mod.write_text(open(TREE_SRC).read())
+    r = subprocess.run([sys.executable, "-c", _TREE_RUNNER, str(mod),
+                        os.path.join(ROOT, "tests", "test_oracle_prefix_tree.py")],
+                       cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:]
