@@ -91,14 +91,27 @@ typedef struct rpkv_shape {
                                 8192)                                           */
   int32_t split_min_keys;    /* tuning: smallest split-KV chunk in keys
                                 (default 64; rounded up to 32)                  */
+  int32_t prefix_detect_keys;/* cascade: when > 0, a batch planned with a host
+                                page table and no cascade hints gets its
+                                shared-prefix tree from the page-table rows;
+                                a level is kept only if it adds at least this
+                                many keys to its parent level (0: off)          */
 } rpkv_shape;
 
-/* Cascade hint: requests [first_req, first_req + num_reqs) of the batch have
- * identical page ids in their first prefix_len / page_size columns
- * (prefix_len must be a multiple of page_size).  The shared prefix is then read
+/* Cascade hint (SGLang source walkthrough "Attention backends", 3.3 "Cascade
+ * Inference": a shared prefix is attended once and merged with each request's
+ * own part by log-sum-exp; the multi-level form takes one level per depth of the
+ * radix tree).  Requests [first_req, first_req + num_reqs) of the batch have
+ * identical page ids in their first prefix_len / page_size columns (prefix_len a
+ * multiple of page_size; 0 makes the hint a no-op).  The shared prefix is read
  * once for all eligible members and merged with each member's own tail.  A member
  * is eligible if it is decode-type and none of its new tokens lies in the prefix
- * (L - n >= prefix_len); other members are computed without the cascade. */
+ * (L - n >= prefix_len); other members are computed without the cascade.
+ * Hints may nest to form several levels: a hint whose range lies inside another's
+ * must have a longer prefix, and its members then attend only the keys between
+ * the two prefixes at that level.  Ranges that overlap without nesting are an
+ * error.  A level with fewer than two eligible members is skipped (its nested
+ * levels attach to the next level up). */
 typedef struct rpkv_prefix_group {
   int32_t first_req;
   int32_t num_reqs;
@@ -122,6 +135,9 @@ typedef struct rpkv_plan_info {
   int32_t decode_chunk;        /* split-KV chunk in keys                  */
   int32_t cascade_members;     /* requests served through the cascade     */
   double plan_host_us;         /* host time of the last plan              */
+  int32_t num_cascade_levels;  /* shared-prefix levels (tree nodes)       */
+  int32_t cascade_depth;       /* longest chain of nested levels          */
+  int32_t num_cascade_level_members; /* sum of the levels' member counts  */
 } rpkv_plan_info;
 
 /* Kernel timing (benchmarks): per kernel kind, launches and summed durations
@@ -179,8 +195,11 @@ void rpkv_plan_destroy(rpkv_plan *plan);
  *                      ceil(L_i / page_size) <= cols <= max_pages_per_req
  *   page_table_host    optional host copy [batch, cols] (row stride = cols); when
  *                      given, page ids are checked to be in [0, num_pages) and
- *                      cascade hints are checked against it
- *   groups_host        optional cascade hints [num_groups]
+ *                      cascade hints are checked against it; with no hints and
+ *                      shape.prefix_detect_keys > 0 the shared-prefix levels
+ *                      are found from it (radix tree of the eligible requests'
+ *                      page ids over their pages cached before this step)
+ *   groups_host        optional cascade hints [num_groups], possibly nested
  * Errors: INVALID_ARG (rule broken), CAPACITY (capacities exceeded). */
 rpkv_status rpkv_plan_batch(rpkv_plan *plan, int32_t batch, const int32_t *cu_seqlens_q_host,
                             const int32_t *cache_seqlens_host, int32_t page_table_cols,
@@ -264,6 +283,18 @@ rpkv_status rpkv_plan_get_items(const rpkv_plan *plan, int32_t kind, int32_t *it
  * addressed by the tile's token-list offset). */
 rpkv_status rpkv_plan_get_token_list(const rpkv_plan *plan, int32_t *out_host, int32_t capacity,
                                      int32_t *count);
+
+/* Host copy of the last plan's shared-prefix levels (from hints or detected),
+ * parents before children.  Level k: parent_host[k] (index of the enclosing
+ * level or -1), prefix_host[k] (shared keys [0, prefix)), and its member requests
+ * members_host[member_indptr_host[k] .. member_indptr_host[k+1]) in ascending
+ * order.  Sizes come from rpkv_plan_get_info: num_cascade_levels (arrays of
+ * that many entries, member_indptr_host one more) and num_cascade_level_members.
+ * Errors: CAPACITY if max_levels or max_members is too small (nothing written). */
+rpkv_status rpkv_plan_get_cascade_tree(const rpkv_plan *plan, int32_t max_levels,
+                                       int32_t max_members, int32_t *parent_host,
+                                       int32_t *prefix_host, int32_t *member_indptr_host,
+                                       int32_t *members_host);
 
 /* ---------------------------------------------------------- once per layer */
 

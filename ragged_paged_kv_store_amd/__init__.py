@@ -34,7 +34,7 @@ EXPORTS = (
     "rpkv_last_indices", "rpkv_plan_get_info", "rpkv_plan_get_items", "rpkv_plan_get_token_list",
     "rpkv_store_kv", "rpkv_attend", "rpkv_forward", "rpkv_timing_enable", "rpkv_timing_collect",
     "rpkv_build_metadata", "rpkv_graph_decode_init", "rpkv_graph_decode_forward",
-    "rpkv_prepare_metadata_csr", "rpkv_rewrite_block_table",
+    "rpkv_prepare_metadata_csr", "rpkv_rewrite_block_table", "rpkv_plan_get_cascade_tree",
 )
 
 
@@ -50,7 +50,8 @@ class Shape(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("num_pages", ctypes.c_int64), ("max_tokens", ctypes.c_int64),
                 ("max_pages_per_req", ctypes.c_int32), ("decode_max_rows", ctypes.c_int32),
-                ("split_target", ctypes.c_int32), ("split_min_keys", ctypes.c_int32)]
+                ("split_target", ctypes.c_int32), ("split_min_keys", ctypes.c_int32),
+                ("prefix_detect_keys", ctypes.c_int32)]
 
 
 class PrefixGroup(ctypes.Structure):
@@ -65,7 +66,8 @@ class PlanInfo(ctypes.Structure):
                 ("num_cascade_items", ctypes.c_int32), ("num_merge_tokens", ctypes.c_int32),
                 ("num_partials", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("decode_chunk", ctypes.c_int32), ("cascade_members", ctypes.c_int32),
-                ("plan_host_us", ctypes.c_double)]
+                ("plan_host_us", ctypes.c_double), ("num_cascade_levels", ctypes.c_int32),
+                ("cascade_depth", ctypes.c_int32), ("num_cascade_level_members", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -95,6 +97,7 @@ def _load():
         "rpkv_plan_get_info": (i32, [vp, P(PlanInfo)]),
         "rpkv_plan_get_items": (i32, [vp, i32, vp, i32, P(i32)]),
         "rpkv_plan_get_token_list": (i32, [vp, vp, i32, P(i32)]),
+        "rpkv_plan_get_cascade_tree": (i32, [vp, i32, i32, vp, vp, vp, vp]),
         "rpkv_store_kv": (i32, [vp, vp, vp, vp, i64, vp, vp, vp]),
         "rpkv_attend": (i32, [vp, vp, vp, vp, vp, ctypes.c_float, vp]),
         "rpkv_forward": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp]),
@@ -202,9 +205,11 @@ def supports(**kw) -> Tuple[bool, str]:
 
 def make_shape(num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int, dtype: int,
                max_batch: int, num_pages: int, max_tokens: int, max_pages_per_req: int,
-               decode_max_rows: int = 0, split_target: int = 0, split_min_keys: int = 0) -> Shape:
+               decode_max_rows: int = 0, split_target: int = 0, split_min_keys: int = 0,
+               prefix_detect_keys: int = 0) -> Shape:
     return Shape(num_q_heads, num_kv_heads, head_dim, page_size, dtype, max_batch, num_pages,
-                 max_tokens, max_pages_per_req, decode_max_rows, split_target, split_min_keys)
+                 max_tokens, max_pages_per_req, decode_max_rows, split_target, split_min_keys,
+                 prefix_detect_keys)
 
 
 class Plan:
@@ -382,6 +387,20 @@ class Plan:
         out = np.zeros(max(n.value, 1), np.int32)
         _check(lib.rpkv_plan_get_token_list(self._h, out.ctypes.data, n.value, ctypes.byref(n)))
         return out[:n.value]
+
+    def cascade_tree(self) -> list:
+        """The last plan's shared-prefix levels, parents first: a list of dicts
+        {"members": tuple of request indices, "prefix": keys, "parent": index or -1}."""
+        inf = self.info()
+        nl, nm = inf["num_cascade_levels"], inf["num_cascade_level_members"]
+        par = np.zeros(max(nl, 1), np.int32)
+        pre = np.zeros(max(nl, 1), np.int32)
+        ind = np.zeros(nl + 1, np.int32)
+        mem = np.zeros(max(nm, 1), np.int32)
+        _check(lib.rpkv_plan_get_cascade_tree(self._h, nl, nm, par.ctypes.data, pre.ctypes.data,
+                                              ind.ctypes.data, mem.ctypes.data))
+        return [{"members": tuple(int(x) for x in mem[ind[k]:ind[k + 1]]),
+                 "prefix": int(pre[k]), "parent": int(par[k])} for k in range(nl)]
 
     def last_indices(self) -> np.ndarray:
         out = np.zeros(max(self.batch, 1), np.int32)

@@ -399,6 +399,36 @@ rpkv_status rpkv_plan_get_info(const rpkv_plan *p, rpkv_plan_info *info) {
   info->decode_chunk = hp.decode_chunk;
   info->cascade_members = hp.cascade_members;
   info->plan_host_us = hp.plan_us;
+  info->num_cascade_levels = (int32_t)hp.tree.size();
+  info->cascade_depth = hp.cascade_depth;
+  int64_t nm = 0;
+  for (const rpkv::CascNode &nd : hp.tree) nm += (int64_t)nd.members.size();
+  info->num_cascade_level_members = (int32_t)nm;
+  return RPKV_OK;
+}
+
+rpkv_status rpkv_plan_get_cascade_tree(const rpkv_plan *p, int32_t max_levels, int32_t max_members,
+                                       int32_t *parent, int32_t *prefix, int32_t *indptr,
+                                       int32_t *members) {
+  if (!p || max_levels < 0 || max_members < 0)
+    return fail(RPKV_ERR_INVALID_ARG, "bad arguments to rpkv_plan_get_cascade_tree");
+  if (!p->planned) return fail(RPKV_ERR_NOT_PREPARED, "no planned batch");
+  const std::vector<rpkv::CascNode> &tree = p->hp.tree;
+  int64_t nm = 0;
+  for (const rpkv::CascNode &nd : tree) nm += (int64_t)nd.members.size();
+  if ((int64_t)tree.size() > max_levels || nm > max_members)
+    return fail(RPKV_ERR_CAPACITY, "cascade tree has " + std::to_string(tree.size()) +
+                                       " levels and " + std::to_string(nm) + " member entries");
+  if (!indptr || (!tree.empty() && (!parent || !prefix || !members)))
+    return fail(RPKV_ERR_INVALID_ARG, "output arrays must be non-NULL");
+  int32_t o = 0;
+  indptr[0] = 0;
+  for (size_t k = 0; k < tree.size(); ++k) {
+    parent[k] = tree[k].parent;
+    prefix[k] = tree[k].prefix;
+    for (int32_t j : tree[k].members) members[o++] = j;
+    indptr[k + 1] = o;
+  }
   return RPKV_OK;
 }
 

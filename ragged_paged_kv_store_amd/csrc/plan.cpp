@@ -79,7 +79,7 @@ rpkv_status check_shape(const rpkv_shape *s, Shape *o, std::string *msg) {
     return RPKV_ERR_INVALID_ARG;
   }
   if (s->decode_max_rows < 0 || s->decode_max_rows > kDecodeRows || s->split_target < 0 ||
-      s->split_min_keys < 0) {
+      s->split_min_keys < 0 || s->prefix_detect_keys < 0) {
     *msg = "tuning fields out of range (decode_max_rows <= 16, others >= 0)";
     return RPKV_ERR_INVALID_ARG;
   }
@@ -97,6 +97,7 @@ rpkv_status check_shape(const rpkv_shape *s, Shape *o, std::string *msg) {
   o->decode_max_rows = s->decode_max_rows ? s->decode_max_rows : kDecodeRows;
   o->split_target = s->split_target ? s->split_target : 8192;
   o->split_min_keys = (int32_t)round_up(s->split_min_keys ? s->split_min_keys : 64, kDecodeKeys);
+  o->prefix_detect_keys = s->prefix_detect_keys;
   return RPKV_OK;
 }
 
@@ -181,6 +182,121 @@ std::vector<Item> xcd_order(const std::vector<Item> &items, const std::vector<in
   return out;
 }
 
+// A candidate level: positions [lb, lb + cnt) of a request order share `prefix`
+// keys.
+struct Span {
+  int32_t lb, cnt, prefix;
+};
+
+// Shared-prefix detection (SGLang walkthrough "Attention backends", 3.2: the
+// radix cache fills the page table, so requests that reuse a cached prefix carry
+// its page ids; 3.3: the multi-level cascade takes one level per depth of the
+// radix tree).  Request j offers its first offered(j) page ids -- the pages whose
+// keys were all cached before this step.  The radix tree of the offered
+// sequences is grown top-down: a group of requests known to agree on `depth` ids
+// extends `depth` while all of them agree on the next id (that depth, in keys,
+// is the group's shared prefix and the group a candidate level if it is not the
+// root), then splits by the next id, requests whose sequence ends there leaving
+// the group; each part of two or more is grown the same way.  The work is the
+// number of (member, shared page) pairs plus a sort at each branch point.
+// Candidates are spans of `order`, which ends up grouped by tree position.
+template <class Offered>
+void detect_shared_prefixes(int32_t P, int32_t batch, int32_t cols, const int32_t *pt,
+                            Offered offered, std::vector<int32_t> *order,
+                            std::vector<Span> *spans) {
+  std::vector<int32_t> len(batch, 0);
+  order->clear();
+  for (int32_t j = 0; j < batch; ++j) {
+    len[j] = std::min(offered(j), cols);
+    if (len[j] > 0) order->push_back(j);
+  }
+  std::vector<int32_t> &ord = *order;
+  auto id_at = [&](int32_t j, int32_t d) {  // -1 once the sequence has ended
+    return d < len[j] ? pt[(int64_t)j * cols + d] : -1;
+  };
+  struct Group {
+    int32_t lb, ub, depth;
+  };
+  std::vector<Group> work;
+  if (ord.size() >= 2) work.push_back(Group{0, (int32_t)ord.size(), 0});
+  while (!work.empty()) {
+    Group g = work.back();
+    work.pop_back();
+    for (;;) {
+      const int32_t id = id_at(ord[g.lb], g.depth);
+      if (id < 0) break;
+      int32_t k = g.lb + 1;
+      while (k < g.ub && id_at(ord[k], g.depth) == id) ++k;
+      if (k < g.ub) break;
+      ++g.depth;
+    }
+    if (g.depth > 0) spans->push_back(Span{g.lb, g.ub - g.lb, g.depth * P});
+    std::sort(ord.begin() + g.lb, ord.begin() + g.ub, [&](int32_t a, int32_t b) {
+      const int32_t ia = id_at(a, g.depth), ib = id_at(b, g.depth);
+      return ia != ib ? ia < ib : a < b;
+    });
+    // parts in reverse so the stack grows them in order (parents before children)
+    for (int32_t e = g.ub; e > g.lb;) {
+      int32_t b = e - 1;
+      const int32_t id = id_at(ord[b], g.depth);
+      while (b > g.lb && id_at(ord[b - 1], g.depth) == id) --b;
+      if (id >= 0 && e - b >= 2) work.push_back(Group{b, e, g.depth + 1});
+      e = b;
+    }
+  }
+}
+
+// Turns candidate levels into the level tree.  Candidates must nest (a range
+// inside another has a longer prefix; ranges may not overlap otherwise).  A
+// candidate becomes a level when at least two of its requests are eligible for
+// its prefix and it adds at least min_keys keys to the nearest level above it;
+// otherwise its nested candidates attach to that level.  Levels come out parents
+// first, members ascending.
+template <class Eligible>
+rpkv_status nest_levels(std::vector<Span> spans, const std::vector<int32_t> &order,
+                        Eligible eligible, int32_t min_keys, std::vector<CascNode> *tree,
+                        std::string *msg) {
+  std::sort(spans.begin(), spans.end(), [](const Span &a, const Span &b) {
+    if (a.lb != b.lb) return a.lb < b.lb;
+    if (a.cnt != b.cnt) return a.cnt > b.cnt;
+    return a.prefix < b.prefix;
+  });
+  struct Open {
+    int32_t end, prefix, level;  // level: nearest level at or above, or -1
+  };
+  std::vector<Open> st;
+  tree->clear();
+  for (const Span &sp : spans) {
+    while (!st.empty() && st.back().end <= sp.lb) st.pop_back();
+    const int32_t end = sp.lb + sp.cnt;
+    int32_t above = -1;
+    if (!st.empty()) {
+      if (end > st.back().end) {
+        *msg = "cascade groups overlap without nesting (at request order position " +
+               std::to_string(sp.lb) + ")";
+        return RPKV_ERR_INVALID_ARG;
+      }
+      if (sp.prefix <= st.back().prefix) {
+        *msg = "a nested cascade group needs a longer prefix than the group enclosing it";
+        return RPKV_ERR_INVALID_ARG;
+      }
+      above = st.back().level;
+    }
+    const int32_t base = above >= 0 ? (*tree)[above].prefix : 0;
+    std::vector<int32_t> members;
+    for (int32_t k = sp.lb; k < end; ++k)
+      if (eligible(order[k], sp.prefix)) members.push_back(order[k]);
+    int32_t level = above;
+    if (members.size() >= 2 && sp.prefix - base >= min_keys) {
+      std::sort(members.begin(), members.end());
+      tree->push_back(CascNode{above, sp.prefix, std::move(members)});
+      level = (int32_t)tree->size() - 1;
+    }
+    st.push_back(Open{end, sp.prefix, level});
+  }
+  return RPKV_OK;
+}
+
 }  // namespace
 
 rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, const int32_t *L,
@@ -247,7 +363,6 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
         }
       }
   }
-  std::vector<int32_t> in_group(batch, -1);
   for (int32_t g = 0; g < ngroups; ++g) {
     const rpkv_prefix_group &gr = groups[g];
     if (gr.first_req < 0 || gr.num_reqs < 0 || (int64_t)gr.first_req + gr.num_reqs > batch ||
@@ -256,20 +371,20 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
              " out of range or prefix_len not a multiple of page_size";
       return RPKV_ERR_INVALID_ARG;
     }
+    if (!pt_host || gr.prefix_len == 0) continue;
+    int32_t ref = -1;  // first member holding the whole prefix
     for (int32_t j = gr.first_req; j < gr.first_req + gr.num_reqs; ++j) {
-      if (in_group[j] >= 0) {
-        *msg = "cascade groups overlap at request " + std::to_string(j);
-        return RPKV_ERR_INVALID_ARG;
+      if (L[j] < gr.prefix_len) continue;
+      if (ref < 0) {
+        ref = j;
+        continue;
       }
-      in_group[j] = g;
-      if (pt_host && L[j] >= gr.prefix_len) {
-        for (int64_t c = 0; c < gr.prefix_len / s.P; ++c)
-          if (pt_host[(int64_t)j * cols + c] != pt_host[(int64_t)gr.first_req * cols + c]) {
-            *msg = "cascade group " + std::to_string(g) + ": request " + std::to_string(j) +
-                   " does not share the prefix pages";
-            return RPKV_ERR_INVALID_ARG;
-          }
-      }
+      for (int64_t c = 0; c < gr.prefix_len / s.P; ++c)
+        if (pt_host[(int64_t)j * cols + c] != pt_host[(int64_t)ref * cols + c]) {
+          *msg = "cascade group " + std::to_string(g) + ": request " + std::to_string(j) +
+                 " does not share the prefix pages";
+          return RPKV_ERR_INVALID_ARG;
+        }
     }
   }
 
@@ -292,19 +407,38 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
     return n_of(i) > 0 && (int64_t)n_of(i) * G <= s.decode_max_rows;
   };
 
-  // cascade eligibility: decode-type members whose new tokens lie past the prefix
-  std::vector<std::vector<int32_t>> casc(ngroups);
-  std::vector<char> is_member(batch, 0);
-  for (int32_t g = 0; g < ngroups; ++g) {
-    const rpkv_prefix_group &gr = groups[g];
-    if (gr.prefix_len <= 0) continue;
-    std::vector<int32_t> m;
-    for (int32_t j = gr.first_req; j < gr.first_req + gr.num_reqs; ++j)
-      if (is_decode(j) && L[j] - n_of(j) >= gr.prefix_len) m.push_back(j);
-    if (m.size() >= 2) {
-      for (int32_t j : m) is_member[j] = 1;
-      casc[g] = std::move(m);
+  // shared-prefix levels: from the hints, else detected from the page table
+  auto eligible = [&](int32_t j, int32_t prefix) {
+    return is_decode(j) && L[j] - n_of(j) >= prefix;
+  };
+  {
+    std::vector<Span> spans;
+    std::vector<int32_t> order;
+    int32_t min_keys = 1;
+    if (ngroups > 0) {
+      order.resize(batch);
+      std::iota(order.begin(), order.end(), 0);
+      for (int32_t g = 0; g < ngroups; ++g)
+        if (groups[g].num_reqs > 0 && groups[g].prefix_len > 0)
+          spans.push_back(Span{groups[g].first_req, groups[g].num_reqs, groups[g].prefix_len});
+    } else if (s.prefix_detect_keys > 0 && pt_host) {
+      detect_shared_prefixes(s.P, batch, cols, pt_host, [&](int32_t j) {
+        return is_decode(j) ? (L[j] - n_of(j)) / s.P : 0;
+      }, &order, &spans);
+      min_keys = s.prefix_detect_keys;
     }
+    rpkv_status st = nest_levels(spans, order, eligible, min_keys, &p.tree, msg);
+    if (st != RPKV_OK) return st;
+  }
+  const int32_t nlev = (int32_t)p.tree.size();
+  std::vector<int32_t> deepest(batch, -1);  // deepest level of each request
+  for (int32_t g = 0; g < nlev; ++g)
+    for (int32_t j : p.tree[g].members) deepest[j] = g;
+  auto own_from = [&](int32_t j) { return deepest[j] >= 0 ? p.tree[deepest[j]].prefix : 0; };
+  for (int32_t g = 0; g < nlev; ++g) {
+    int32_t d = 1;
+    for (int32_t a = p.tree[g].parent; a >= 0; a = p.tree[a].parent) ++d;
+    p.cascade_depth = std::max(p.cascade_depth, d);
   }
 
   std::vector<int32_t> nsplit(T, 1);
@@ -353,31 +487,45 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
     }
   }
 
-  // cascade prefix tiles: all eligible members' rows against the shared keys
-  std::vector<int32_t> casc_npc(ngroups, 0);
-  for (int32_t g = 0; g < ngroups; ++g) {
-    if (casc[g].empty()) continue;
-    const int32_t prefix = groups[g].prefix_len;
-    const int32_t off = (int32_t)p.toklist.size();
-    for (int32_t j : casc[g])
-      for (int32_t t = cu[j]; t < cu[j + 1]; ++t) p.toklist.push_back(t);
-    const int32_t nt = (int32_t)p.toklist.size() - off;
-    const int32_t ntile = (int32_t)cdiv(nt, tpt);
-    // prefix chunks: enough tiles to spread over the chip, chunks >= 256 keys
-    int64_t npc = cdiv(512, (int64_t)ntile * s.Hkv);
-    npc = std::max<int64_t>(1, std::min<int64_t>(npc, prefix / 256));
-    const int32_t pchunk = (int32_t)round_up(cdiv(prefix, npc), kPrefillKeys);
-    npc = cdiv(prefix, pchunk);
-    casc_npc[g] = (int32_t)npc;
-    for (int32_t h = 0; h < s.Hkv; ++h)
-      for (int32_t tl = 0; tl < ntile; ++tl)
-        for (int32_t c = 0; c < npc; ++c) {
-          const int32_t a = tl * tpt, b = std::min(nt, a + tpt);
-          pre.push_back(Item{casc[g][0], h, off + a, b - a, -1, c * pchunk,
-                             std::min(prefix, (c + 1) * pchunk), c});
-          pre_key.push_back(((int64_t)batch + g) * s.Hkv + h);
-          ++p.n_cascade_items;
-        }
+  // level tiles: each level's members stacked against the keys it adds.  One
+  // chunk length for all levels, sized so the levels give about kPrefillSlots
+  // tiles in all (chunks of at least 256 keys); a member's partials are numbered
+  // along its path from the top level down, then its tail.
+  std::vector<int32_t> lev_npc(nlev, 0), lev_off(nlev, 0), lev_tok(nlev, 0);
+  {
+    int64_t work = 0;
+    for (int32_t g = 0; g < nlev; ++g) {
+      const CascNode &nd = p.tree[g];
+      lev_tok[g] = (int32_t)p.toklist.size();
+      for (int32_t j : nd.members)
+        for (int32_t t = cu[j]; t < cu[j + 1]; ++t) p.toklist.push_back(t);
+      const int32_t nt = (int32_t)p.toklist.size() - lev_tok[g];
+      const int32_t base = nd.parent >= 0 ? p.tree[nd.parent].prefix : 0;
+      work += cdiv(nt, tpt) * s.Hkv * (int64_t)(nd.prefix - base);
+    }
+    const int64_t lchunk = std::max<int64_t>(256, round_up(cdiv(work, kPrefillSlots), kPrefillKeys));
+    for (int32_t g = 0; g < nlev; ++g) {
+      const CascNode &nd = p.tree[g];
+      const int32_t base = nd.parent >= 0 ? p.tree[nd.parent].prefix : 0;
+      const int32_t seg = nd.prefix - base;
+      int64_t npc = cdiv(seg, lchunk);
+      const int32_t pchunk = (int32_t)round_up(cdiv(seg, npc), kPrefillKeys);
+      npc = cdiv(seg, pchunk);
+      lev_npc[g] = (int32_t)npc;
+      lev_off[g] = nd.parent >= 0 ? lev_off[nd.parent] + lev_npc[nd.parent] : 0;
+      const int32_t off = lev_tok[g];
+      const int32_t nt = (g + 1 < nlev ? lev_tok[g + 1] : (int32_t)p.toklist.size()) - off;
+      const int32_t ntile = (int32_t)cdiv(nt, tpt);
+      for (int32_t h = 0; h < s.Hkv; ++h)
+        for (int32_t tl = 0; tl < ntile; ++tl)
+          for (int32_t c = 0; c < npc; ++c) {
+            const int32_t a = tl * tpt, b = std::min(nt, a + tpt);
+            pre.push_back(Item{nd.members[0], h, off + a, b - a, -1, base + c * pchunk,
+                               std::min(nd.prefix, base + (c + 1) * pchunk), lev_off[g] + c});
+            pre_key.push_back(((int64_t)batch + g) * s.Hkv + h);
+            ++p.n_cascade_items;
+          }
+    }
   }
 
   // split-KV chunk: one length for the batch, sized for ~split_target items.
@@ -387,7 +535,7 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
   int64_t dec_keys = 0;
   for (int32_t i = 0; i < batch; ++i) {
     if (!is_decode(i)) continue;
-    dec_keys += (int64_t)(is_member[i] ? L[i] - groups[in_group[i]].prefix_len : L[i]) * s.Hkv;
+    dec_keys += (int64_t)(L[i] - own_from(i)) * s.Hkv;
   }
   int64_t chunk64 =
       std::max<int64_t>(s.split_min_keys, round_up(cdiv(dec_keys, s.split_target), kDecodeKeys));
@@ -406,7 +554,7 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
 
   // decode-type requests outside any cascade
   for (int32_t i = 0; i < batch; ++i) {
-    if (!is_decode(i) || is_member[i]) continue;
+    if (!is_decode(i) || deepest[i] >= 0) continue;
     const int32_t n = n_of(i);
     const int32_t ns = (int32_t)cdiv(L[i], chunk);
     for (int32_t t = cu[i]; t < cu[i + 1]; ++t) nsplit[t] = ns;
@@ -418,21 +566,19 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
                            ns > 1 ? c : -1});
   }
 
-  // cascade tails: each member's own keys past the prefix
-  for (int32_t g = 0; g < ngroups; ++g) {
-    if (casc[g].empty()) continue;
-    const int32_t prefix = groups[g].prefix_len;
-    const int32_t npc = casc_npc[g];
-    for (int32_t j : casc[g]) {
-      const int32_t n = n_of(j);
-      const int32_t ns = (int32_t)cdiv(L[j] - prefix, chunk);
-      for (int32_t t = cu[j]; t < cu[j + 1]; ++t) nsplit[t] = npc + ns;
-      for (int32_t c = 0; c < ns; ++c)
-        for (int32_t h = 0; h < s.Hkv; ++h)
-          dec.push_back(Item{j, h, cu[j], n, L[j] - n, prefix + c * chunk,
-                             std::min(L[j], prefix + (c + 1) * chunk), npc + c});
-      ++p.cascade_members;
-    }
+  // cascade tails: each member's own keys past its deepest level
+  for (int32_t j = 0; j < batch; ++j) {
+    const int32_t g = deepest[j];
+    if (g < 0) continue;
+    const int32_t prefix = p.tree[g].prefix, first = lev_off[g] + lev_npc[g];
+    const int32_t n = n_of(j);
+    const int32_t ns = (int32_t)cdiv(L[j] - prefix, chunk);
+    for (int32_t t = cu[j]; t < cu[j + 1]; ++t) nsplit[t] = first + ns;
+    for (int32_t c = 0; c < ns; ++c)
+      for (int32_t h = 0; h < s.Hkv; ++h)
+        dec.push_back(Item{j, h, cu[j], n, L[j] - n, prefix + c * chunk,
+                           std::min(L[j], prefix + (c + 1) * chunk), first + c});
+    ++p.cascade_members;
   }
 
   // partials and merge list

@@ -42,6 +42,16 @@ constexpr int kPrefillSlots = 512;    // MI355X: 256 CUs x 2 resident prefill ti
 // 64-key step (measured rates: ~2.5 us per tile step, ~20 keys/us per chunk)
 constexpr int kConcurrentKeysPerStep = 24;
 
+// One level of the shared-prefix tree.  Its members attend the keys between the
+// parent level's prefix (0 at the top) and `prefix` once, stacked together in
+// MFMA tiles over the first member's page-table row; the keys past the deepest
+// level a member belongs to are its own tail.
+struct CascNode {
+  int32_t parent;  // index of the enclosing level, -1 at the top
+  int32_t prefix;  // shared keys [0, prefix), a multiple of the page size
+  std::vector<int32_t> members;  // request indices, >= 2
+};
+
 struct HostPlan {
   int32_t batch = 0, T = 0, max_q = 0, max_k = 0;
   std::vector<int32_t> cu_q, L;
@@ -51,6 +61,8 @@ struct HostPlan {
   std::vector<int32_t> tok_pbase;  // [T] partial base or -1
   std::vector<int32_t> merge;      // [M][3] token, partial base, count
   std::vector<int32_t> toklist;    // cascade token lists
+  std::vector<CascNode> tree;      // shared-prefix levels, parents first
+  int32_t cascade_depth = 0;
   int64_t n_partials = 0;
   int32_t n_cascade_items = 0, cascade_members = 0, decode_chunk = 0;
   int32_t n_prefill_real = 0;      // items before padding
@@ -60,7 +72,7 @@ struct HostPlan {
 struct Shape {
   int32_t Hq, Hkv, D, P, log2P, dtype, max_batch, max_pages_per_req;
   int64_t num_pages, max_tokens;
-  int32_t decode_max_rows, split_target, split_min_keys;
+  int32_t decode_max_rows, split_target, split_min_keys, prefix_detect_keys;
   int32_t G() const { return Hq / Hkv; }
 };
 

@@ -140,6 +140,16 @@ def test_cascade_hint_checked_against_host_table(rp):
         p.plan_host([0, 1, 2, 3], [40, 40, 40], 3, pt, groups=[(0, 2, 20)])
     with pytest.raises(rp.RpkvError):   # overlapping groups
         p.plan_host([0, 1, 2, 3], [40, 40, 40], 3, pt, groups=[(0, 2, 16), (1, 2, 16)])
+    # nested groups form two levels
+    pt = np.array([[1, 2, 3], [1, 2, 4], [1, 9, 5]], np.int32)
+    p.plan_host([0, 1, 2, 3], [40, 40, 40], 3, pt, groups=[(0, 3, 16), (0, 2, 32)])
+    assert p.cascade_tree() == [{"members": (0, 1, 2), "prefix": 16, "parent": -1},
+                                {"members": (0, 1), "prefix": 32, "parent": 0}]
+    assert p.info()["cascade_depth"] == 2
+    with pytest.raises(rp.RpkvError):   # nested without a longer prefix
+        p.plan_host([0, 1, 2, 3], [40, 40, 40], 3, pt, groups=[(0, 3, 16), (0, 2, 16)])
+    with pytest.raises(rp.RpkvError):   # nested level's pages differ
+        p.plan_host([0, 1, 2, 3], [40, 40, 40], 3, pt, groups=[(0, 3, 16), (1, 2, 32)])
 
 
 # ------------------------------------------------------------------ coverage
@@ -175,6 +185,11 @@ def check_coverage(rp, plan, spec):
                     hi = min(kend, a + 1)
                 else:
                     assert kend - 1 <= a, "cascade tile covers a key a row cannot see"
+                    # the tile reads request `req`'s pages: every row's request
+                    # must hold the same pages for those keys
+                    pk = np.arange(kbeg // spec.P, (kend - 1) // spec.P + 1)
+                    assert (spec.page_table[req, pk] == spec.page_table[i, pk]).all(), \
+                        "cascade tile reads pages a row's request does not share"
                     hi = kend
                 assert kend <= int(spec.L[i]) or pos0 < 0
                 for g in range(G):

@@ -218,6 +218,86 @@ def c5_shared_prefix(seed: int = 4, prefix: int = 8192, tail=(64, 1024), n_share
                  shared=(list(range(n_share)), prefix), groups=groups)
 
 
+def radix_tree(seed: int = 5, bs: int = 128, levels=((1, 4096), (8, 2048), (4, 1024)),
+               tail=(64, 512), shuffle: bool = True, Hq: int = 32, Hkv: int = 8, P: int = 16,
+               extra_prefills=(), name: str = "radix_tree_decode") -> BatchSpec:
+    """Decodes whose prefixes form a radix tree of shared pages (several sharing
+    levels, as when a system prompt, per-task instructions and per-branch context
+    are reused): level d splits every node of level d-1 into `fanout` children,
+    each adding `keys` shared keys (a multiple of P).  The bs requests are dealt
+    evenly to the leaves in tree order; each gets its own tail of U[tail] keys
+    (the decoded token is the tail's last).  Every tree node's pages are allocated
+    once from the shuffled pool (1.1x of the unique pages) and repeated in the rows
+    of the requests under it.  shuffle=True permutes the request order, so members
+    of a node are not contiguous; otherwise cascade hints (first_req, num_reqs,
+    prefix_len) are returned for every node, nested.  extra_prefills: (cached,
+    new) pairs appended as prefill-type requests with unshared pages."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nleaf = int(np.prod([f for f, _ in levels])) if levels else 1
+    assert bs % nleaf == 0 and all(k % P == 0 for _, k in levels)
+    per_leaf = bs // nleaf
+    t = _u(rng, tail[0], tail[1], bs)
+    n = [1] * bs + [int(b) for _, b in extra_prefills]
+    L = [sum(k for _, k in levels) + int(x) for x in t] + [int(a) + int(b) for a, b in extra_prefills]
+    # tree nodes in depth-first order: (depth, first request, count)
+    nodes = []
+
+    def walk(d, first, count):
+        if d == len(levels):
+            return
+        f = levels[d][0]
+        for c in range(f):
+            sub = count // f
+            nodes.append((d, first + c * sub, sub))
+            walk(d + 1, first + c * sub, sub)
+    walk(0, 0, bs)
+    own = [-(-int(l) // P) for l in L]
+    for (d, first, count) in nodes:
+        for j in range(first, first + count):
+            own[j] -= levels[d][1] // P
+    unique = sum(levels[d][1] // P for d, _, _ in nodes) + sum(own)
+    num_pages = max(int(np.ceil(unique * 1.1)), 1)
+    perm = rng.permutation(num_pages).astype(np.int32)
+    W = max(-(-int(l) // P) for l in L)
+    table = np.zeros((len(L), W), dtype=np.int32)
+    fill = [0] * len(L)
+    cursor = 0
+    for (d, first, count) in nodes:
+        np_ = levels[d][1] // P
+        ids = perm[cursor:cursor + np_]
+        cursor += np_
+        for j in range(first, first + count):
+            table[j, fill[j]:fill[j] + np_] = ids
+            fill[j] += np_
+    for j in range(len(L)):
+        need = -(-int(L[j]) // P) - fill[j]
+        table[j, fill[j]:fill[j] + need] = perm[cursor:cursor + need]
+        cursor += need
+    assert cursor <= num_pages
+    prefix_at = np.cumsum([0] + [k for _, k in levels])
+    groups = [(first, count, int(prefix_at[d + 1])) for (d, first, count) in nodes
+              if count >= 1]
+    if shuffle:
+        order = np.concatenate([rng.permutation(bs), np.arange(bs, len(L))]).astype(np.int64)
+        table = table[order]
+        n = [n[i] for i in order]
+        L = [L[i] for i in order]
+        groups = []
+    return build(name, "bf16", Hq, Hkv, 128, P, n, L, seed, rng, 1.1, groups=groups,
+                 table=table, num_pages=num_pages)
+
+
+def radix_tree_small(seed: int = 15, shuffle: bool = True, P: int = 16, Hq: int = 32,
+                     Hkv: int = 8, extra_prefills=(), levels=None) -> BatchSpec:
+    """Reduced twin of radix_tree: 16 decodes, levels of 256 / 2x128 / 2x64 keys
+    (scaled to the page size), tails U[5, 40]."""
+    if levels is None:
+        levels = ((1, max(256, 4 * P)), (2, max(128, 2 * P)), (2, max(64, P)))
+    return radix_tree(seed=seed, bs=16, levels=levels, tail=(5, 40), shuffle=shuffle, Hq=Hq,
+                      Hkv=Hkv, P=P, extra_prefills=extra_prefills,
+                      name="radix_tree_decode_small")
+
+
 def full_config(cid: int) -> BatchSpec:
     """The five workloads at their stated sizes (seeds 0..4)."""
     return {1: c1_tiny, 2: c2_llama8b_mixed, 3: c3_decode_heavy, 4: c4_chunked_prefill,
