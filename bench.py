@@ -13,7 +13,9 @@ Default workload: the Llama-3-8B-shaped mixed layer (Hq=32, Hkv=8, D=128,
 page_size=16; query lens [2000, 512, 1 x 6]; decode histories uniform in
 [512, 4096]); value = algorithmic attention TFLOP/s (unmasked query-key pairs x
 4 x D x Hq) over the whole step.  --workload picks another of the five batches
-(the decode-heavy one reports KV-read GB/s).
+(the decode-heavy one reports KV-read GB/s); --workload radix runs 128 decodes
+under a three-level shared-prefix tree whose levels the planner finds from the
+page table each step, and also times the same steps with the levels off.
 
 Prints ONE JSON line (rank 0) with the roofline of the dominant kernel, measured
 with HIP events on the launch stream in a second pass over the same steps, and
@@ -46,14 +48,20 @@ WORKLOADS = {
               "Hq=28 Hkv=4 D=128 page_size=16, bf16"),
     "c5": (5, "c5_shared_prefix_cascade: 64 decodes sharing an 8192-token prefix, tails U[64,1024], "
               "+ 2 x (28672 cached + 4096 new), Hq=64 Hkv=8 D=128 page_size=16, bf16"),
+    "radix": (0, "radix_tree_decode: 128 decodes under a 3-level prefix tree (4096 keys shared "
+                 "by all, 8 x 2048, 4 x 1024 per branch), tails U[64,512], shuffled order, "
+                 "levels detected from the page table (>= 256 keys), Hq=32 Hkv=8 D=128 "
+                 "page_size=16, bf16"),
 }
+RADIX_DETECT_KEYS = 256
 
 
-def algorithmic(spec, plan_info_members: int):
+def algorithmic(spec, tree):
     """Algorithmic work of one layer, split by kernel.
 
     flops = 4*D*Hq*sum over requests of [n(L-n) + n(n+1)/2] (unmasked pairs).
-    KV bytes = 2*Hkv*D*b per unique slot read (a cascade's shared prefix once).
+    KV bytes = 2*Hkv*D*b per unique slot read: a shared-prefix level's keys once
+    for all its members.  `tree` is the plan's list of levels.
     """
     D, Hq, Hkv, b = spec.D, spec.Hq, spec.Hkv, spec.elem_bytes
     n = spec.n.astype(np.int64)
@@ -61,30 +69,28 @@ def algorithmic(spec, plan_info_members: int):
     pairs = n * (L - n) + n * (n + 1) // 2
     G = spec.G
     dec = (n > 0) & (n * G <= 16)
-    member = np.zeros(spec.bs, bool)
-    prefix = np.zeros(spec.bs, np.int64)
-    for (f, c, pl) in spec.groups:
-        for j in range(f, f + c):
-            if dec[j] and L[j] - n[j] >= pl:
-                member[j] = True
-                prefix[j] = pl
-    if plan_info_members == 0:
-        member[:] = False
-        prefix[:] = 0
+    own_from = np.zeros(spec.bs, np.int64)   # first key of each request's own tail
+    level_pairs = 0
+    shared = 0                               # key reads the levels save
+    for nd in tree:
+        base = tree[nd["parent"]]["prefix"] if nd["parent"] >= 0 else 0
+        seg = nd["prefix"] - base
+        m = list(nd["members"])
+        level_pairs += seg * int(n[m].sum())
+        shared += seg * (len(m) - 1)
+        own_from[m] = np.maximum(own_from[m], nd["prefix"])
     row_kv = 2 * Hkv * D * b
     flops_total = 4 * D * Hq * int(pairs.sum())
-    flops_prefill = 4 * D * Hq * int(pairs[~dec].sum() + (n * prefix)[member].sum())
-    dec_keys = int(np.where(member, L - prefix, L)[dec].sum())
+    flops_prefill = 4 * D * Hq * (int(pairs[~dec].sum()) + level_pairs)
+    dec_keys = int((L - own_from)[dec].sum())
     kv_decode = row_kv * dec_keys
-    uniq = int(L.sum())
-    for (f, c, pl) in spec.groups:
-        uniq -= pl * (int(member[f:f + c].sum()) - 1) if member[f:f + c].sum() > 1 else 0
-    kv_total = row_kv * uniq
+    kv_total = row_kv * (int(L.sum()) - shared)
     T = spec.T
     io = T * spec.Hq * D * b * 2 + T * Hkv * D * b * 2 * 2   # q read, out write, k/v read + pool write
     store_bytes = T * Hkv * D * b * 2 * 2
     return dict(flops_total=flops_total, flops_prefill=flops_prefill, kv_decode=kv_decode,
-                kv_total=kv_total, bytes_total=kv_total + io, store_bytes=store_bytes)
+                kv_total=kv_total, bytes_total=kv_total + io, store_bytes=store_bytes,
+                all_decode=bool(dec.all()))
 
 
 def kernel_sources_hash() -> str:
@@ -233,7 +239,8 @@ def main():
 
     cid, desc = WORKLOADS[args.workload]
     layers = args.layers
-    spec = synth.full_config(cid)
+    radix = args.workload == "radix"
+    spec = synth.radix_tree() if radix else synth.full_config(cid)
     stream = torch.cuda.current_stream()
 
     # per-layer buffers: q/k/v/out per layer, pools cycled over npools sets
@@ -256,10 +263,12 @@ def main():
     outs = [torch.empty_like(layer0.q) for _ in range(nq)]
     pt = layer0.page_table
     sm = layer0.slot_mapping
-    plan = H.make_plan(spec)
+    # the radix workload's levels are found from the host page table each step
+    plan = H.make_plan(spec, prefix_detect_keys=RADIX_DETECT_KEYS if radix else 0)
+    pt_host = spec.page_table if radix else None
 
     def step():
-        plan.prepare(spec.cu_q, spec.L, pt, None, spec.groups, stream=stream)
+        plan.prepare(spec.cu_q, spec.L, pt, pt_host, spec.groups, stream=stream)
         for l in range(layers):
             kp, vp = pools[l % npools]
             q, k, v = qkv[l % nq]
@@ -311,7 +320,7 @@ def main():
         gtimes = gplan.timing_collect()
         gplan.timing_enable(False)
         torch.cuda.synchronize()
-        alg = algorithmic(spec, 0)
+        alg = algorithmic(spec, [])
         dec_n, dec_ms = gtimes["decode"]
         kv_rate = alg["kv_total"] * layers / (graph_ms * 1e-3) / 1e9
         avg_s = dec_ms / dec_n * 1e-3
@@ -356,10 +365,10 @@ def main():
     plan.timing_enable(False)
     torch.cuda.synchronize()
 
-    alg = algorithmic(spec, info["cascade_members"])
+    alg = algorithmic(spec, plan.cascade_tree())
     per_kernel = {k: {"launches": n, "avg_us": (ms * 1e3 / n) if n else None}
                   for k, (n, ms) in times.items()}
-    decode_heavy = alg["flops_prefill"] == 0 and spec.dtype == "bf16"
+    decode_heavy = alg["all_decode"] and spec.dtype == "bf16"
     if decode_heavy:
         metric_value = alg["kv_total"] * layers / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
@@ -370,7 +379,12 @@ def main():
     dom = max((k for k in times if times[k][0]), key=lambda k: times[k][1])
     n_l, ms_l = times[dom]
     avg_s = ms_l / n_l * 1e-3
-    if dom in ("prefill", "fused"):
+    if dom == "fused" and decode_heavy:
+        # decodes only: the launch streams every unique KV byte of the layer
+        # (shared-prefix levels once, tails per request)
+        roof = dict(bound="hbm", achieved=alg["kv_total"] / avg_s / 1e9, peak=PEAK_HBM_GBPS,
+                    unit="GB/s")
+    elif dom in ("prefill", "fused"):
         # the fused launch also streams the split-KV chunks; only the tiles'
         # algorithmic FLOPs are credited
         roof = dict(bound="mfma", achieved=alg["flops_prefill"] / avg_s / 1e12,
@@ -387,6 +401,28 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = dom
     roof["traffic"] = measured_traffic(args.workload, dom) if layers == LAYERS else None
+
+    flat = None
+    if radix:
+        # the same steps with the levels off: every request streams its whole prefix
+        fplan = H.make_plan(spec)
+
+        def fstep():
+            fplan.prepare(spec.cu_q, spec.L, pt, None, [], stream=stream)
+            for l in range(layers):
+                kp, vp = pools[l % npools]
+                q, k, v = qkv[l % nq]
+                fplan.forward(q, k, v, sm, kp, vp, outs[l % nq], spec.scale, stream=stream)
+        for _ in range(args.warmup):
+            fstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fstep()
+        torch.cuda.synchronize()
+        flat_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        flat = {"ms_per_step": round(flat_ms, 4), "speedup_with_levels": round(flat_ms / ms_per_step, 3),
+                "kv_bytes_per_layer": int(algorithmic(spec, [])["kv_total"])}
 
     meta_us = metadata_build_us(spec, layer0, rp, torch)
     cpu = None
@@ -426,6 +462,8 @@ def main():
             "algorithmic_per_layer": alg,
             "plan": info,
             "metadata_build_us": meta_us,
+            "without_cascade_levels": flat,
+            "cascade_tree": {"levels": info["num_cascade_levels"], "depth": info["cascade_depth"]},
         },
     }
     print(json.dumps(line), flush=True)
