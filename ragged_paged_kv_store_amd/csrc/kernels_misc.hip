@@ -51,51 +51,60 @@ int launch_store_kv(const void *k, const void *v, const int32_t *slots, int64_t 
 // A partial with l_s = -inf carries no weight.  One wavefront per (token, head):
 // lane s holds partial s's weight (64 partials per pass), each lane D/64
 // channels; the partial rows are independent loads issued back to back.
+// All of a (token, head)'s log-sum-exps and partial rows requested at once (one
+// memory round trip after the merge record), then combined; for ns <= NF.
+template <int D, int NF>
+__device__ __forceinline__ void merge_all_at_once(int32_t pb, int32_t ns, int h, int lane,
+                                                  int64_t ob, const float *__restrict__ o_part,
+                                                  const float *__restrict__ lse_part,
+                                                  void *__restrict__ out, int32_t Hq,
+                                                  int32_t dtype) {
+  constexpr int PER = D / 64;
+  const float *op = o_part + ((int64_t)pb * Hq + h) * D + lane * PER;
+  const int64_t stride = (int64_t)Hq * D;
+  const float lv = lane < ns ? lse_part[(int64_t)(pb + lane) * Hq + h] : kNegInf;
+  float v[NF][PER];
+#pragma unroll
+  for (int u = 0; u < NF; ++u)
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[u][j] = u < ns ? op[u * stride + j] : 0.f;
+  float M = lv;
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
+  const float wl = M == kNegInf ? 0.f : fast_exp2(lv - M);  // 2^-inf = 0
+  float W = 0.f, acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+#pragma unroll
+  for (int u = 0; u < NF; ++u) {
+    const float w = __shfl(wl, u, 64);
+    W += w;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] += w * v[u][j];
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  if (dtype == RPKV_F32) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) ((float *)out)[ob + j] = acc[j] * inv;
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) ((uint16_t *)out)[ob + j] = f32_to_bf16(acc[j] * inv);
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void merge_one(int32_t tok, int32_t pb, int32_t ns,
                                           const float *__restrict__ o_part,
                                           const float *__restrict__ lse_part,
                                           void *__restrict__ out, int32_t Hq, int32_t dtype) {
   constexpr int PER = D / 64;
-  constexpr int kFast = 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.y * 4 + wave;
   if (h >= Hq) return;
   const int64_t ob = ((int64_t)tok * Hq + h) * D + lane * PER;
-  if (ns <= kFast) {
-    // the usual case: every log-sum-exp and partial row is requested at once
-    // (one memory round trip after the merge record), then combined
-    const float *op = o_part + ((int64_t)pb * Hq + h) * D + lane * PER;
-    const int64_t stride = (int64_t)Hq * D;
-    const float lv = lane < ns ? lse_part[(int64_t)(pb + lane) * Hq + h] : kNegInf;
-    float v[kFast][PER];
-#pragma unroll
-    for (int u = 0; u < kFast; ++u)
-#pragma unroll
-      for (int j = 0; j < PER; ++j) v[u][j] = u < ns ? op[u * stride + j] : 0.f;
-    float M = lv;
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
-    const float wl = M == kNegInf ? 0.f : fast_exp2(lv - M);  // 2^-inf = 0
-    float W = 0.f, acc[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-#pragma unroll
-    for (int u = 0; u < kFast; ++u) {
-      const float w = __shfl(wl, u, 64);
-      W += w;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) acc[j] += w * v[u][j];
-    }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
-    if (dtype == RPKV_F32) {
-#pragma unroll
-      for (int j = 0; j < PER; ++j) ((float *)out)[ob + j] = acc[j] * inv;
-    } else {
-#pragma unroll
-      for (int j = 0; j < PER; ++j) ((uint16_t *)out)[ob + j] = f32_to_bf16(acc[j] * inv);
-    }
-    return;
-  }
+  // the usual cases: everything requested at once
+  if (ns <= 8) return merge_all_at_once<D, 8>(pb, ns, h, lane, ob, o_part, lse_part, out, Hq, dtype);
+  if (ns <= 32)
+    return merge_all_at_once<D, 32>(pb, ns, h, lane, ob, o_part, lse_part, out, Hq, dtype);
   float M = kNegInf;
   for (int s0 = 0; s0 < ns; s0 += 64)
     if (s0 + lane < ns) M = fmaxf(M, lse_part[(int64_t)(pb + s0 + lane) * Hq + h]);

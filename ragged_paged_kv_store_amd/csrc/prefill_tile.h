@@ -88,6 +88,9 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
   const int qh = it.kvh * G + gg;
   const int apos = casc ? INT32_MAX : it.pos0 + tl;
   const int amin = casc ? INT32_MAX : it.pos0;  // smallest position in the tile
+  // partial index base of this row's token, requested now and first used by the
+  // epilogue (so the epilogue does not wait on a load)
+  const int32_t pbase = it.split >= 0 ? a.tok_pbase[tok] : 0;
 
   bf16x8 qf[8];
   {
@@ -335,7 +338,7 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
         *(u32x2 *)(orow + 32 * db + 8 * g4 + 4 * half) = w;
       }
   } else {
-    const int64_t pi = (int64_t)a.tok_pbase[tok] + it.split;
+    const int64_t pi = (int64_t)pbase + it.split;
     float *prow = a.o_part + (pi * a.Hq + qh) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
