@@ -145,3 +145,30 @@ def test_full_size_radix_tree_sampled_rows():
     assert np.array_equal(H.to_host_bits(spec, kp_gpu), kp_ref)
     assert np.array_equal(H.to_host_bits(spec, vp_gpu), vp_ref)
     assert bool(torch.isfinite(out.float()).all())
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_f32_levels(D):
+    """fp32 batches: the levels run on the fp32 tiles (16 rows) and split-KV path."""
+    spec = synth.radix_tree_small(seed=70 + D, shuffle=True, dtype="f32", D=D)
+    plan, _ = check(spec, prefix_detect_keys=1)
+    assert plan.info()["cascade_depth"] == 3
+
+
+def test_csr_page_table_detects_the_same_levels():
+    """With the page table in CSR form (and its host copy) the planner finds the
+    same levels and the outputs are bit-identical to the dense table's."""
+    from tests.test_gpu_page_formats import bits, to_csr
+    spec = synth.radix_tree_small(seed=72, shuffle=True)
+    ht = synth.host_tensors(spec)
+    out_dense, p1 = H.gpu_forward(spec, H.dev_batch(spec, ht), groups=[], prefix_detect_keys=1)
+    db = H.dev_batch(spec, ht)
+    indptr, indices, last = to_csr(spec)
+    plan = H.make_plan(spec, prefix_detect_keys=1)
+    plan.prepare_csr(spec.cu_q, indptr, last, torch.from_numpy(indices).cuda(), indices)
+    out = torch.full_like(db.q, float("nan"))
+    plan.forward(db.q, db.k, db.v, db.slot_mapping, db.kpool, db.vpool, out, spec.scale)
+    torch.cuda.synchronize()
+    assert pt.canonical(plan.cascade_tree()) == pt.canonical(p1.cascade_tree())
+    assert plan.info()["cascade_depth"] == 3
+    assert torch.equal(bits(out), bits(out_dense))

@@ -220,7 +220,8 @@ def c5_shared_prefix(seed: int = 4, prefix: int = 8192, tail=(64, 1024), n_share
 
 def radix_tree(seed: int = 5, bs: int = 128, levels=((1, 4096), (8, 2048), (4, 1024)),
                tail=(64, 512), shuffle: bool = True, Hq: int = 32, Hkv: int = 8, P: int = 16,
-               extra_prefills=(), name: str = "radix_tree_decode") -> BatchSpec:
+               extra_prefills=(), name: str = "radix_tree_decode", dtype: str = "bf16",
+               D: int = 128) -> BatchSpec:
     """Decodes whose prefixes form a radix tree of shared pages (several sharing
     levels, as when a system prompt, per-task instructions and per-branch context
     are reused): level d splits every node of level d-1 into `fanout` children,
@@ -283,19 +284,20 @@ def radix_tree(seed: int = 5, bs: int = 128, levels=((1, 4096), (8, 2048), (4, 1
         n = [n[i] for i in order]
         L = [L[i] for i in order]
         groups = []
-    return build(name, "bf16", Hq, Hkv, 128, P, n, L, seed, rng, 1.1, groups=groups,
+    return build(name, dtype, Hq, Hkv, D, P, n, L, seed, rng, 1.1, groups=groups,
                  table=table, num_pages=num_pages)
 
 
 def radix_tree_small(seed: int = 15, shuffle: bool = True, P: int = 16, Hq: int = 32,
-                     Hkv: int = 8, extra_prefills=(), levels=None) -> BatchSpec:
+                     Hkv: int = 8, extra_prefills=(), levels=None, dtype: str = "bf16",
+                     D: int = 128) -> BatchSpec:
     """Reduced twin of radix_tree: 16 decodes, levels of 256 / 2x128 / 2x64 keys
     (scaled to the page size), tails U[5, 40]."""
     if levels is None:
         levels = ((1, max(256, 4 * P)), (2, max(128, 2 * P)), (2, max(64, P)))
     return radix_tree(seed=seed, bs=16, levels=levels, tail=(5, 40), shuffle=shuffle, Hq=Hq,
                       Hkv=Hkv, P=P, extra_prefills=extra_prefills,
-                      name="radix_tree_decode_small")
+                      name="radix_tree_decode_small", dtype=dtype, D=D)
 
 
 def full_config(cid: int) -> BatchSpec:
