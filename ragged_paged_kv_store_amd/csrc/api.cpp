@@ -32,6 +32,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct rpkv_plan {
   Shape s{};
   HostPlan hp;
+  HostPlan hp_next;  // planned into, then swapped with hp when the batch is valid
   bool planned = false;
   bool prepared = false;
   int device = -1;
@@ -160,12 +161,13 @@ rpkv_status rpkv_plan_batch(rpkv_plan *p, int32_t batch, const int32_t *cu, cons
   std::string msg;
   rpkv_status st;
   try {
-    st = rpkv::plan_batch_host(p->s, batch, cu, seqlens, cols, pt_host, groups, ngroups, &p->hp,
-                               &msg);
+    st = rpkv::plan_batch_host(p->s, batch, cu, seqlens, cols, pt_host, groups, ngroups,
+                               &p->hp_next, &msg);
   } catch (const std::bad_alloc &) {
     return fail(RPKV_ERR_CAPACITY, "host allocation failed while planning");
   }
   if (st != RPKV_OK) return fail(st, msg);
+  std::swap(p->hp, p->hp_next);
   p->planned = true;
   p->ws_need = workspace_need(p);
   return RPKV_OK;

@@ -112,14 +112,28 @@ int64_t item_work(const Item &it) {
 // stay on one XCD, groups larger than a fair share are cut into contiguous
 // pieces, pieces are placed longest-first on the least loaded queue, each queue
 // runs longest-first, and the queues are interleaved so block b runs on XCD b%8.
-std::vector<Item> xcd_order(const std::vector<Item> &items, const std::vector<int64_t> &gkey) {
-  std::vector<Item> out;
-  if (items.empty()) return out;
-  std::vector<size_t> idx(items.size());
+void xcd_order(const std::vector<Item> &items, const std::vector<int64_t> &gkey,
+               std::vector<Item> *outp) {
+  std::vector<Item> &out = *outp;
+  out.clear();
+  if (items.empty()) return;
+  const size_t n = items.size();
+  std::vector<int64_t> work(n);
+  for (size_t k = 0; k < n; ++k) work[k] = item_work(items[k]);
+  // items sharing K/V together, in ascending key order (the planner emits them
+  // that way, so this is usually the identity); ties keep the input order
+  std::vector<size_t> idx(n);
   std::iota(idx.begin(), idx.end(), 0);
-  std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return gkey[a] < gkey[b]; });
+  if (!std::is_sorted(gkey.begin(), gkey.end()))
+    std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return gkey[a] < gkey[b]; });
+  // dense rank of each item's key (ascending keys -> ascending ranks)
+  std::vector<uint32_t> grank(n);
+  for (size_t k = 0, r = 0; k < n; ++k) {
+    if (k > 0 && gkey[idx[k]] != gkey[idx[k - 1]]) ++r;
+    grank[idx[k]] = (uint32_t)r;
+  }
   int64_t total = 0;
-  for (auto &it : items) total += item_work(it);
+  for (int64_t w : work) total += w;
   const int64_t share = std::max<int64_t>(1, cdiv(total, kNumXcd));
   struct Piece {
     std::vector<size_t> members;
@@ -127,17 +141,17 @@ std::vector<Item> xcd_order(const std::vector<Item> &items, const std::vector<in
   };
   std::vector<Piece> pieces;
   size_t i = 0;
-  while (i < idx.size()) {
+  while (i < n) {
     size_t j = i;
     int64_t gw = 0;
-    while (j < idx.size() && gkey[idx[j]] == gkey[idx[i]]) gw += item_work(items[idx[j++]]);
+    while (j < n && gkey[idx[j]] == gkey[idx[i]]) gw += work[idx[j++]];
     const int64_t npieces = std::max<int64_t>(1, cdiv(gw, share));
     const int64_t per = cdiv(gw, npieces);
     Piece cur;
     for (size_t k = i; k < j; ++k) {
       cur.members.push_back(idx[k]);
-      cur.work += item_work(items[idx[k]]);
-      if (cur.work >= per && (int64_t)pieces.size() < INT32_MAX) {
+      cur.work += work[idx[k]];
+      if (cur.work >= per) {
         pieces.push_back(std::move(cur));
         cur = Piece();
       }
@@ -145,33 +159,42 @@ std::vector<Item> xcd_order(const std::vector<Item> &items, const std::vector<in
     if (!cur.members.empty()) pieces.push_back(std::move(cur));
     i = j;
   }
-  std::stable_sort(pieces.begin(), pieces.end(),
-                   [](const Piece &a, const Piece &b) { return a.work > b.work; });
+  std::vector<size_t> porder(pieces.size());
+  std::iota(porder.begin(), porder.end(), 0);
+  std::sort(porder.begin(), porder.end(), [&](size_t a, size_t b) {
+    return pieces[a].work != pieces[b].work ? pieces[a].work > pieces[b].work : a < b;
+  });
   std::vector<std::vector<size_t>> q(kNumXcd);
   std::vector<int64_t> load(kNumXcd, 0);
-  for (auto &p : pieces) {
+  for (size_t pi : porder) {
+    Piece &p = pieces[pi];
     int best = (int)(std::min_element(load.begin(), load.end()) - load.begin());
     load[best] += p.work;
-    std::stable_sort(p.members.begin(), p.members.end(), [&](size_t a, size_t b) {
-      return item_work(items[a]) > item_work(items[b]);
-    });
     q[best].insert(q[best].end(), p.members.begin(), p.members.end());
   }
   // Within a queue: longest first by coarse work bucket (eighths of the queue's
   // longest item), and inside a bucket tiles sharing K/V together, so nearly
   // equal tiles of one group run side by side and their K/V stays in the XCD's
-  // L2, while very unequal tiles still start longest first.
+  // L2, while very unequal tiles still start longest first.  (The members of a
+  // piece were appended in group order; the sort key decides everything else.)
+  // The order is packed into one 64-bit key per item (bucket descending, key rank
+  // ascending, work descending) with the item index as the final tie-break.
   size_t qlen = 0;
+  std::vector<std::pair<uint64_t, uint32_t>> keyed;
   for (auto &qq : q) {
     int64_t mx = 1;
-    for (size_t k : qq) mx = std::max(mx, item_work(items[k]));
-    auto bucket = [&](size_t k) { return item_work(items[k]) * 8 / (mx + 1); };
-    std::stable_sort(qq.begin(), qq.end(), [&](size_t a, size_t b) {
-      const int64_t ba = bucket(a), bb = bucket(b);
-      if (ba != bb) return ba > bb;
-      if (gkey[a] != gkey[b]) return gkey[a] < gkey[b];
-      return item_work(items[a]) > item_work(items[b]);
-    });
+    for (size_t k : qq) mx = std::max(mx, work[k]);
+    keyed.clear();
+    keyed.reserve(qq.size());
+    for (size_t k : qq) {
+      const uint64_t b = (uint64_t)(work[k] * 8 / (mx + 1));  // 0..7
+      const uint64_t w = (uint64_t)std::min<int64_t>(work[k], 0xFFFFFFFF);
+      keyed.emplace_back(((7 - b) << 60) | ((uint64_t)std::min<uint32_t>(grank[k], 0x0FFFFFFF) << 32) |
+                             (0xFFFFFFFF - w),
+                         (uint32_t)k);
+    }
+    std::sort(keyed.begin(), keyed.end());
+    for (size_t k = 0; k < qq.size(); ++k) qq[k] = keyed[k].second;
     qlen = std::max(qlen, qq.size());
   }
   Item pad{};
@@ -179,7 +202,6 @@ std::vector<Item> xcd_order(const std::vector<Item> &items, const std::vector<in
   out.assign(qlen * kNumXcd, pad);
   for (int x = 0; x < kNumXcd; ++x)
     for (size_t k = 0; k < q[x].size(); ++k) out[k * kNumXcd + x] = items[q[x][k]];
-  return out;
 }
 
 // A candidate level: positions [lb, lb + cnt) of a request order share `prefix`
@@ -303,7 +325,8 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
                             int32_t cols, const int32_t *pt_host, const rpkv_prefix_group *groups,
                             int32_t ngroups, HostPlan *out, std::string *msg) {
   auto t_start = std::chrono::steady_clock::now();
-  HostPlan p;
+  HostPlan &p = *out;  // the caller's scratch plan; on an error its contents are unspecified
+  p.reset();
   // ------------------------------------------------------------ validation
   if (batch < 0) {
     *msg = "batch must be >= 0";
@@ -431,7 +454,8 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
     if (st != RPKV_OK) return st;
   }
   const int32_t nlev = (int32_t)p.tree.size();
-  std::vector<int32_t> deepest(batch, -1);  // deepest level of each request
+  std::vector<int32_t> &deepest = p.tmp.deepest;  // deepest level of each request
+  deepest.assign(batch, -1);
   for (int32_t g = 0; g < nlev; ++g)
     for (int32_t j : p.tree[g].members) deepest[j] = g;
   auto own_from = [&](int32_t j) { return deepest[j] >= 0 ? p.tree[deepest[j]].prefix : 0; };
@@ -441,13 +465,28 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
     p.cascade_depth = std::max(p.cascade_depth, d);
   }
 
-  std::vector<int32_t> nsplit(T, 1);
-  std::vector<Item> pre, dec;
-  std::vector<int64_t> pre_key;  // K/V-sharing group key per prefill item
+  std::vector<int32_t> &nsplit = p.tmp.nsplit;
+  nsplit.assign(T, 1);
+  std::vector<Item> &pre = p.tmp.pre, &dec = p.tmp.dec;
+  std::vector<int64_t> &pre_key = p.tmp.pre_key;  // K/V-sharing group key per prefill item
+  pre.clear();
+  dec.clear();
+  pre_key.clear();
 
   // prefill-type requests: tiles of tpt tokens x G heads of one KV head
-  std::vector<Item> tiles;
-  std::vector<int64_t> tile_key;
+  std::vector<Item> &tiles = p.tmp.tiles;
+  std::vector<int64_t> &tile_key = p.tmp.tile_key;
+  tiles.clear();
+  tile_key.clear();
+  {
+    int64_t nt = 0;
+    for (int32_t i = 0; i < batch; ++i)
+      if (n_of(i) > 0 && !is_decode(i)) nt += cdiv(n_of(i), tpt) * s.Hkv;
+    tiles.reserve(nt);
+    tile_key.reserve(nt);
+    pre.reserve(nt + nt / 2);
+    pre_key.reserve(nt + nt / 2);
+  }
   int64_t total_steps = 0;
   for (int32_t i = 0; i < batch; ++i) {
     const int32_t n = n_of(i);
@@ -552,33 +591,48 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
   const int32_t chunk = (int32_t)std::min<int64_t>(chunk64, 1 << 30);
   p.decode_chunk = chunk;
 
-  // decode-type requests outside any cascade
-  for (int32_t i = 0; i < batch; ++i) {
-    if (!is_decode(i) || deepest[i] >= 0) continue;
-    const int32_t n = n_of(i);
-    const int32_t ns = (int32_t)cdiv(L[i], chunk);
-    for (int32_t t = cu[i]; t < cu[i + 1]; ++t) nsplit[t] = ns;
-    // KV heads innermost: the heads of one chunk read interleaved rows of the
-    // same pages at about the same time
-    for (int32_t c = 0; c < ns; ++c)
-      for (int32_t h = 0; h < s.Hkv; ++h)
-        dec.push_back(Item{i, h, cu[i], n, L[i] - n, c * chunk, std::min(L[i], (c + 1) * chunk),
-                           ns > 1 ? c : -1});
-  }
-
-  // cascade tails: each member's own keys past its deepest level
-  for (int32_t j = 0; j < batch; ++j) {
-    const int32_t g = deepest[j];
-    if (g < 0) continue;
-    const int32_t prefix = p.tree[g].prefix, first = lev_off[g] + lev_npc[g];
-    const int32_t n = n_of(j);
-    const int32_t ns = (int32_t)cdiv(L[j] - prefix, chunk);
-    for (int32_t t = cu[j]; t < cu[j + 1]; ++t) nsplit[t] = first + ns;
-    for (int32_t c = 0; c < ns; ++c)
-      for (int32_t h = 0; h < s.Hkv; ++h)
-        dec.push_back(Item{j, h, cu[j], n, L[j] - n, prefix + c * chunk,
-                           std::min(L[j], prefix + (c + 1) * chunk), first + c});
-    ++p.cascade_members;
+  // Split-KV items.  Longest first (the launch runs them in order): every full
+  // chunk has the longest length, so those go out in generation order and only
+  // the shorter last chunks (one per request and KV head) are sorted.  Written
+  // through raw pointers into vectors sized up front.
+  {
+    int64_t nfull = 0, nlast = 0;
+    for (int32_t i = 0; i < batch; ++i) {
+      if (!is_decode(i)) continue;
+      const int32_t keys = L[i] - own_from(i);
+      nfull += (int64_t)(keys / chunk) * s.Hkv;
+      nlast += keys % chunk ? s.Hkv : 0;
+    }
+    std::vector<Item> &last = p.tmp.dlast;
+    dec.resize(nfull);
+    last.resize(nlast);
+    Item *wf = dec.data(), *wl = last.data();
+    const int32_t Hkv = s.Hkv;
+    for (int32_t i = 0; i < batch; ++i) {
+      if (!is_decode(i)) continue;
+      const int32_t g = deepest[i];
+      // outside any cascade: all keys, partials 0..; else the keys past the
+      // deepest level, partials after that level's
+      const int32_t from = g >= 0 ? p.tree[g].prefix : 0;
+      const int32_t first = g >= 0 ? lev_off[g] + lev_npc[g] : 0;
+      const int32_t n = n_of(i), Li = L[i], c0 = cu[i];
+      const int32_t ns = (int32_t)cdiv(Li - from, chunk);
+      for (int32_t t = c0; t < cu[i + 1]; ++t) nsplit[t] = first + ns;
+      const bool single = g < 0 && ns == 1;  // the whole range in one item: final output
+      // KV heads innermost: the heads of one chunk read interleaved rows of the
+      // same pages at about the same time
+      for (int32_t c = 0; c < ns; ++c) {
+        const int32_t kb = from + c * chunk, ke = std::min(Li, kb + chunk);
+        Item *&w = ke - kb == chunk ? wf : wl;
+        for (int32_t h = 0; h < Hkv; ++h)
+          *w++ = Item{i, h, c0, n, Li - n, kb, ke, single ? -1 : first + c};
+      }
+      if (g >= 0) ++p.cascade_members;
+    }
+    std::stable_sort(last.begin(), last.end(), [](const Item &x, const Item &y) {
+      return (x.kend - x.kbeg) > (y.kend - y.kbeg);
+    });
+    dec.insert(dec.end(), last.begin(), last.end());
   }
 
   // partials and merge list
@@ -603,17 +657,13 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
   if (f32) {
     std::stable_sort(pre.begin(), pre.end(),
                      [](const Item &a, const Item &b) { return item_work(a) > item_work(b); });
-    p.prefill = std::move(pre);
+    std::swap(p.prefill, pre);
   } else {
-    p.prefill = xcd_order(pre, pre_key);
+    xcd_order(pre, pre_key, &p.prefill);
   }
-  std::stable_sort(dec.begin(), dec.end(), [](const Item &a, const Item &b) {
-    return (a.kend - a.kbeg) > (b.kend - b.kbeg);
-  });
-  p.decode = std::move(dec);
+  std::swap(p.decode, dec);
   p.plan_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_start)
                   .count();
-  *out = std::move(p);
   return RPKV_OK;
 }
 

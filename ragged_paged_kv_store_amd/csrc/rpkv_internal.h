@@ -52,6 +52,15 @@ struct CascNode {
   std::vector<int32_t> members;  // request indices, >= 2
 };
 
+// Work buffers of the planner, kept with a plan so their capacity carries over
+// from batch to batch (a fresh multi-hundred-KB vector per batch costs page
+// faults on every plan).
+struct PlanScratch {
+  std::vector<Item> tiles, pre, dec, dlast;
+  std::vector<int64_t> tile_key, pre_key;
+  std::vector<int32_t> nsplit, deepest;
+};
+
 struct HostPlan {
   int32_t batch = 0, T = 0, max_q = 0, max_k = 0;
   std::vector<int32_t> cu_q, L;
@@ -67,6 +76,18 @@ struct HostPlan {
   int32_t n_cascade_items = 0, cascade_members = 0, decode_chunk = 0;
   int32_t n_prefill_real = 0;      // items before padding
   double plan_us = 0;
+  PlanScratch tmp;
+  // empty the plan, keeping every vector's capacity
+  void reset() {
+    batch = T = max_q = max_k = 0;
+    cu_q.clear(); L.clear(); csr_indptr.clear(); prefill.clear(); decode.clear();
+    tok_pbase.clear(); merge.clear(); toklist.clear(); tree.clear();
+    cascade_depth = 0;
+    n_partials = 0;
+    n_cascade_items = cascade_members = decode_chunk = 0;
+    n_prefill_real = 0;
+    plan_us = 0;
+  }
 };
 
 struct Shape {
@@ -79,7 +100,8 @@ struct Shape {
 // Validate a shape; on failure returns the status and fills msg.
 rpkv_status check_shape(const rpkv_shape *s, Shape *out, std::string *msg);
 
-// Build the work partition of one batch on the host.
+// Build the work partition of one batch on the host into *out (emptied first,
+// its vectors' capacity reused; its contents are unspecified after an error).
 rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu,
                             const int32_t *L, int32_t cols, const int32_t *pt_host,
                             const rpkv_prefix_group *groups, int32_t ngroups, HostPlan *out,
