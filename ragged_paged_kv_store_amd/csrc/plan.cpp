@@ -629,10 +629,19 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
       }
       if (g >= 0) ++p.cascade_members;
     }
-    std::stable_sort(last.begin(), last.end(), [](const Item &x, const Item &y) {
-      return (x.kend - x.kbeg) > (y.kend - y.kbeg);
+    // the shorter chunks come in runs of Hkv (one per request): order the runs
+    const int64_t nruns = nlast / Hkv;
+    std::vector<int32_t> &ro = p.tmp.runs;
+    ro.resize(nruns);
+    std::iota(ro.begin(), ro.end(), 0);
+    std::stable_sort(ro.begin(), ro.end(), [&](int32_t x, int32_t y) {
+      return (last[(int64_t)x * Hkv].kend - last[(int64_t)x * Hkv].kbeg) >
+             (last[(int64_t)y * Hkv].kend - last[(int64_t)y * Hkv].kbeg);
     });
-    dec.insert(dec.end(), last.begin(), last.end());
+    dec.resize(nfull + nlast);
+    Item *w = dec.data() + nfull;
+    for (int32_t r : ro)
+      for (int32_t h = 0; h < Hkv; ++h) *w++ = last[(int64_t)r * Hkv + h];
   }
 
   // partials and merge list

@@ -58,7 +58,7 @@ struct CascNode {
 struct PlanScratch {
   std::vector<Item> tiles, pre, dec, dlast;
   std::vector<int64_t> tile_key, pre_key;
-  std::vector<int32_t> nsplit, deepest;
+  std::vector<int32_t> nsplit, deepest, runs;
 };
 
 struct HostPlan {
