@@ -338,8 +338,9 @@ rpkv_status rpkv_forward(rpkv_plan *plan, const void *q, const void *k, const vo
  * seq_lens and slot_mapping on the device), then replay.
  *
  * rpkv_graph_decode_init: fixes the capacities (max_batch requests, q_len new
- * tokens each, lengths up to max_seq_len), picks one key chunk (>= 256 keys, at
- * most 8 chunks per request) and allocates the plan-owned partial workspace.
+ * tokens each, lengths up to max_seq_len), picks one key chunk (>= 256 keys; 2 to
+ * 32 chunks per request, more for small batches) and allocates the plan-owned
+ * partial workspace.
  * Call it outside capture.  bf16 only; q_len * Hq / Hkv <= 16. */
 rpkv_status rpkv_graph_decode_init(rpkv_plan *plan, int32_t max_batch, int32_t q_len,
                                    int32_t max_seq_len);

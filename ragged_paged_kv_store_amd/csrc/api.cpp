@@ -562,10 +562,14 @@ rpkv_status rpkv_graph_decode_init(rpkv_plan *p, int32_t max_batch, int32_t q_le
     return fail(RPKV_ERR_UNSUPPORTED, "q_len * Hq / Hkv must be <= 16 (one split-KV item)");
   if ((int64_t)max_seq_len > (int64_t)p->s.max_pages_per_req * p->s.P)
     return fail(RPKV_ERR_CAPACITY, "max_seq_len exceeds max_pages_per_req * page_size");
-  if ((int64_t)max_batch * q_len > INT32_MAX / 8)
+  if ((int64_t)max_batch * q_len > INT32_MAX / 32)
     return fail(RPKV_ERR_INVALID_ARG, "max_batch * q_len too large");
-  // at most 8 chunks per request (the merge's one-round-trip path), >= 256 keys
-  const int32_t chunk = std::max<int32_t>(256, (int32_t)(((max_seq_len + 7) / 8 + 63) / 64 * 64));
+  // Chunks per request: enough that a full batch gives about 4 wavefronts per
+  // resident slot (2048 on the chip), between 2 and 32 (the merge's
+  // one-round-trip path); chunks of >= 256 keys, a multiple of 64.
+  const int64_t waves_per_chunk = (int64_t)max_batch * p->s.Hkv;
+  const int32_t want = (int32_t)std::min<int64_t>(32, std::max<int64_t>(2, (8192 + waves_per_chunk - 1) / waves_per_chunk));
+  const int32_t chunk = std::max<int32_t>(256, (int32_t)(((max_seq_len + want - 1) / want + 63) / 64 * 64));
   const int32_t maxc = (max_seq_len + chunk - 1) / chunk;
   int dev = 0;
   int e = hipGetDevice(&dev);
