@@ -134,3 +134,39 @@ def test_full_radix_tree_plans(rp):
         p.plan_host(spec.cu_q, spec.L, spec.page_table.shape[1], spec.page_table)
         times.append(p.info()["plan_host_us"])
     assert min(times) < 5000, times
+
+
+def test_cascade_tree_query_errors(rp):
+    """The tree query reports CAPACITY when the arrays are too small, and the
+    detection threshold must be >= 0."""
+    import ctypes
+    spec = synth.radix_tree_small(seed=43, shuffle=True)
+    p, tree = plan_tree(rp, spec, prefix_detect_keys=1)
+    inf = p.info()
+    assert inf["num_cascade_levels"] == len(tree) == 7
+    assert inf["num_cascade_level_members"] == sum(len(nd["members"]) for nd in tree)
+    par = (ctypes.c_int32 * 8)()
+    pre = (ctypes.c_int32 * 8)()
+    ind = (ctypes.c_int32 * 9)()
+    mem = (ctypes.c_int32 * 64)()
+    st = rp.lib.rpkv_plan_get_cascade_tree(p._h, 6, 64, par, pre, ind, mem)
+    assert st == 6  # CAPACITY: 7 levels do not fit 6
+    st = rp.lib.rpkv_plan_get_cascade_tree(p._h, 8, inf["num_cascade_level_members"] - 1,
+                                           par, pre, ind, mem)
+    assert st == 6
+    st = rp.lib.rpkv_plan_get_cascade_tree(p._h, 8, 64, par, pre, ind, mem)
+    assert st == 0 and ind[7] == inf["num_cascade_level_members"]
+    ok, _ = rp.supports(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, dtype=0,
+                        max_batch=4, num_pages=64, max_tokens=64, max_pages_per_req=8,
+                        prefix_detect_keys=-1)
+    assert not ok
+
+
+def test_detection_needs_the_host_table(rp):
+    """Without a host copy of the page table there is nothing to detect from: the
+    batch is planned without levels."""
+    spec = synth.radix_tree_small(seed=44, shuffle=True)
+    p = make_plan(rp, spec, prefix_detect_keys=1)
+    p.plan_host(spec.cu_q, spec.L, spec.page_table.shape[1], None)
+    assert p.cascade_tree() == [] and p.info()["cascade_members"] == 0
+    check_coverage(rp, p, spec)
