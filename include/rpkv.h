@@ -21,9 +21,12 @@
  *    cache update can be a separate call that scatters by slot_mapping.
  *    Step 1: a backend answers capability questions (head sizes, dtypes).
  *  - SGLang source walkthrough "Attention backends", 3.1 (plan once, then run;
- *    a caller-provided device workspace), 3.3 (cascade: a shared prefix attended
- *    once and merged with each request's own tail by log-sum-exp), 6 (a mixed
- *    batch is split by token into decode work and prefill work).
+ *    a caller-provided device workspace), 3.2 (the page table in CSR form; the
+ *    radix cache fills it, so reused prefixes carry the same page ids), 3.3
+ *    (cascade: a shared prefix attended once and merged with each request's own
+ *    tail by log-sum-exp; the multi-level form takes one level per depth of the
+ *    radix tree), 6 (a mixed batch is split by token into decode work and
+ *    prefill work).
  *  - "Variable-length batching and one mixed forward pass", exercise 2: pure
  *    decode work uses split-KV (flash-decoding) kernels; "Source code": the
  *    logits indices are cu_q[1:] - 1.
@@ -128,7 +131,7 @@ typedef struct rpkv_plan_info {
   int32_t max_seqlen_k;
   int32_t num_prefill_items;   /* MFMA tiles, incl. cascade prefix tiles  */
   int32_t num_decode_items;    /* split-KV chunks (one wave each)         */
-  int32_t num_cascade_items;   /* of which shared-prefix tiles            */
+  int32_t num_cascade_items;   /* of which shared-prefix level tiles      */
   int32_t num_merge_tokens;    /* tokens whose heads are merged           */
   int64_t num_partials;        /* partial results (token x split)         */
   int64_t workspace_bytes;     /* device workspace the batch needs        */
@@ -238,7 +241,7 @@ rpkv_status rpkv_prepare_metadata(rpkv_plan *plan, int32_t batch, const int32_t 
  *   last_page_len_host  [batch] host, in [1, page_size] for requests with pages
  *   page_indices_dev    device int32 [page_indptr[batch]]
  *   page_indices_host   optional host copy (page ids then checked, cascade hints
- *                       checked), else NULL
+ *                       checked, shared prefixes detectable), else NULL
  * Other arguments and errors as rpkv_prepare_metadata. */
 rpkv_status rpkv_prepare_metadata_csr(rpkv_plan *plan, int32_t batch,
                                       const int32_t *cu_seqlens_q_host,

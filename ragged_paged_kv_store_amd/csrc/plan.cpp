@@ -15,9 +15,12 @@
 //  * split-KV chunks: one chunk length for the whole batch, chosen ahead of time
 //    so the decode launch has about `split_target` items (vLLM's FlashAttention
 //    metadata carries ahead-of-time scheduler data and a split count);
-//  * cascade: eligible members of a shared-prefix group get prefix tiles that
-//    stack all members' rows against the shared keys, plus their own tail chunks;
-//    the partials are merged by log-sum-exp (SGLang walkthrough 3.3);
+//  * cascade: a tree of shared-prefix levels, from nested hints or found in the
+//    host page table (radix tree of the decode requests' cached page ids); each
+//    level's eligible members are stacked in tiles against the keys the level
+//    adds, each member keeps its own tail chunks, and the partials along a
+//    member's path are merged by log-sum-exp (SGLang walkthrough 3.3; the
+//    multi-level form takes one level per depth of the radix tree);
 //  * partial-result layout and the merge list;
 //  * launch order: prefill tiles that read the same K/V go to the same XCD
 //    (blocks are dealt round-robin to the 8 XCDs, each with its own L2), and
