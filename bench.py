@@ -219,7 +219,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
-              "path shards by request or KV head with no exchange, see DESIGN.md", file=sys.stderr)
+              "path would shard by request or by KV head with no exchange between GPUs",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
