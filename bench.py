@@ -218,7 +218,7 @@ def main():
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+        print(f"bench.py: the library runs on one GPU (asked for --gpus {args.gpus}); the "
               "path would shard by request or by KV head with no exchange between GPUs",
               file=sys.stderr)
         sys.exit(2)
