@@ -99,6 +99,11 @@ typedef struct rpkv_shape {
                                 shared-prefix tree from the page-table rows;
                                 a level is kept only if it adds at least this
                                 many keys to its parent level (0: off)          */
+  int32_t tiles_per_block;   /* tuning: MFMA tiles per workgroup: 1 (four
+                                wavefronts, one tile), 2 (eight wavefronts, two
+                                tiles in ping-pong), 0 (default): 2 when the
+                                batch's tiles average at least 24 key steps of
+                                64, else 1                                      */
 } rpkv_shape;
 
 /* Cascade hint (SGLang source walkthrough "Attention backends", 3.3 "Cascade
@@ -141,6 +146,7 @@ typedef struct rpkv_plan_info {
   int32_t num_cascade_levels;  /* shared-prefix levels (tree nodes)       */
   int32_t cascade_depth;       /* longest chain of nested levels          */
   int32_t num_cascade_level_members; /* sum of the levels' member counts  */
+  int32_t tiles_per_block;     /* MFMA tiles per workgroup this batch     */
 } rpkv_plan_info;
 
 /* Kernel timing (benchmarks): per kernel kind, launches and summed durations

@@ -51,7 +51,7 @@ class Shape(ctypes.Structure):
                 ("num_pages", ctypes.c_int64), ("max_tokens", ctypes.c_int64),
                 ("max_pages_per_req", ctypes.c_int32), ("decode_max_rows", ctypes.c_int32),
                 ("split_target", ctypes.c_int32), ("split_min_keys", ctypes.c_int32),
-                ("prefix_detect_keys", ctypes.c_int32)]
+                ("prefix_detect_keys", ctypes.c_int32), ("tiles_per_block", ctypes.c_int32)]
 
 
 class PrefixGroup(ctypes.Structure):
@@ -67,7 +67,8 @@ class PlanInfo(ctypes.Structure):
                 ("num_partials", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("decode_chunk", ctypes.c_int32), ("cascade_members", ctypes.c_int32),
                 ("plan_host_us", ctypes.c_double), ("num_cascade_levels", ctypes.c_int32),
-                ("cascade_depth", ctypes.c_int32), ("num_cascade_level_members", ctypes.c_int32)]
+                ("cascade_depth", ctypes.c_int32), ("num_cascade_level_members", ctypes.c_int32),
+                ("tiles_per_block", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -206,10 +207,10 @@ def supports(**kw) -> Tuple[bool, str]:
 def make_shape(num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int, dtype: int,
                max_batch: int, num_pages: int, max_tokens: int, max_pages_per_req: int,
                decode_max_rows: int = 0, split_target: int = 0, split_min_keys: int = 0,
-               prefix_detect_keys: int = 0) -> Shape:
+               prefix_detect_keys: int = 0, tiles_per_block: int = 0) -> Shape:
     return Shape(num_q_heads, num_kv_heads, head_dim, page_size, dtype, max_batch, num_pages,
                  max_tokens, max_pages_per_req, decode_max_rows, split_target, split_min_keys,
-                 prefix_detect_keys)
+                 prefix_detect_keys, tiles_per_block)
 
 
 class Plan:

@@ -406,6 +406,7 @@ rpkv_status rpkv_plan_get_info(const rpkv_plan *p, rpkv_plan_info *info) {
   int64_t nm = 0;
   for (const rpkv::CascNode &nd : hp.tree) nm += (int64_t)nd.members.size();
   info->num_cascade_level_members = (int32_t)nm;
+  info->tiles_per_block = hp.tiles_per_block;
   return RPKV_OK;
 }
 
@@ -515,9 +516,9 @@ rpkv_status rpkv_attend(rpkv_plan *p, const void *q, const void *kpool, const vo
   if (p->s.dtype == RPKV_BF16) {
     if (pre.n_items > 0 && dec.n_items > 0)
       st = timed(p, RPKV_KERNEL_FUSED, stream,
-                 [&] { return rpkv::launch_fused_bf16(pre, dec, stream); }, "fused launch");
+                 [&] { return rpkv::launch_fused_bf16(pre, dec, hp.tiles_per_block, stream); }, "fused launch");
     else if (pre.n_items > 0)
-      st = timed(p, RPKV_KERNEL_PREFILL, stream, [&] { return rpkv::launch_prefill_bf16(pre, stream); },
+      st = timed(p, RPKV_KERNEL_PREFILL, stream, [&] { return rpkv::launch_prefill_bf16(pre, hp.tiles_per_block, stream); },
                  "prefill launch");
     else if (dec.n_items > 0)
       st = timed(p, RPKV_KERNEL_DECODE, stream, [&] { return rpkv::launch_decode_bf16(dec, stream); },

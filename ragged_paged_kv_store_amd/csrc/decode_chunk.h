@@ -280,13 +280,13 @@ __device__ __forceinline__ void decode_item(const AttnArgs &a, const Item &it) {
   }
 }
 
-// One wavefront of a 4-wavefront block runs item block*4 + wave of the list.
-template <class Slots>
+// One wavefront of a WPB-wavefront block runs item block*WPB + wave of the list.
+template <class Slots, int WPB = kDecodeWavesPerBlock>
 __device__ __forceinline__ void decode_chunk(const AttnArgs &a, int block) {
   // uniform wavefront index: the item and its page ids are then scalar loads,
   // which do not wait on the vector-load counter of the K/V loads in flight
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ii = block * kDecodeWavesPerBlock + wave;
+  const int ii = block * WPB + wave;
   if (ii >= a.n_items) return;
   const Item it = a.items[ii];
   if (it.ntok == 0) return;

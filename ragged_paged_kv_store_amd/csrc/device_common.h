@@ -53,6 +53,19 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// The two halves of a wavefront exchanged (lane l gets lane l ^ 32) and
+// combined: gfx950's v_permlane32_swap, a VALU instruction (no LDS round
+// trip).  The swap of v with itself leaves {v[l % 32], v[l % 32 + 32]} in
+// the pair on every lane.
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ int32_t clamp_page(int32_t pg, int64_t num_pages) {
   return pg < 0 ? 0 : (pg >= num_pages ? (int32_t)(num_pages - 1) : pg);
 }

@@ -82,8 +82,9 @@ rpkv_status check_shape(const rpkv_shape *s, Shape *o, std::string *msg) {
     return RPKV_ERR_INVALID_ARG;
   }
   if (s->decode_max_rows < 0 || s->decode_max_rows > kDecodeRows || s->split_target < 0 ||
-      s->split_min_keys < 0 || s->prefix_detect_keys < 0) {
-    *msg = "tuning fields out of range (decode_max_rows <= 16, others >= 0)";
+      s->split_min_keys < 0 || s->prefix_detect_keys < 0 || s->tiles_per_block < 0 ||
+      s->tiles_per_block > 2) {
+    *msg = "tuning fields out of range (decode_max_rows <= 16, tiles_per_block <= 2, others >= 0)";
     return RPKV_ERR_INVALID_ARG;
   }
   o->Hq = s->num_q_heads;
@@ -101,6 +102,7 @@ rpkv_status check_shape(const rpkv_shape *s, Shape *o, std::string *msg) {
   o->split_target = s->split_target ? s->split_target : 8192;
   o->split_min_keys = (int32_t)round_up(s->split_min_keys ? s->split_min_keys : 64, kDecodeKeys);
   o->prefix_detect_keys = s->prefix_detect_keys;
+  o->tiles_per_block = s->tiles_per_block;
   return RPKV_OK;
 }
 
@@ -115,7 +117,7 @@ int64_t item_work(const Item &it) {
 // stay on one XCD, groups larger than a fair share are cut into contiguous
 // pieces, pieces are placed longest-first on the least loaded queue, each queue
 // runs longest-first, and the queues are interleaved so block b runs on XCD b%8.
-void xcd_order(const std::vector<Item> &items, const std::vector<int64_t> &gkey,
+void xcd_order(const std::vector<Item> &items, const std::vector<int64_t> &gkey, int per_block,
                std::vector<Item> *outp) {
   std::vector<Item> &out = *outp;
   out.clear();
@@ -200,11 +202,16 @@ void xcd_order(const std::vector<Item> &items, const std::vector<int64_t> &gkey,
     for (size_t k = 0; k < qq.size(); ++k) qq[k] = keyed[k].second;
     qlen = std::max(qlen, qq.size());
   }
+  // workgroup b runs on XCD b % 8 and takes per_block consecutive items:
+  // items k..k+per_block-1 of queue x go to workgroup (k / per_block) * 8 + x
   Item pad{};
   pad.ntok = 0;
+  const size_t per = (size_t)per_block;
+  qlen = (qlen + per - 1) / per * per;
   out.assign(qlen * kNumXcd, pad);
   for (int x = 0; x < kNumXcd; ++x)
-    for (size_t k = 0; k < q[x].size(); ++k) out[k * kNumXcd + x] = items[q[x][k]];
+    for (size_t k = 0; k < q[x].size(); ++k)
+      out[((k / per) * kNumXcd + x) * per + k % per] = items[q[x][k]];
 }
 
 // A candidate level: positions [lb, lb + cnt) of a request order share `prefix`
@@ -670,8 +677,17 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
     std::stable_sort(pre.begin(), pre.end(),
                      [](const Item &a, const Item &b) { return item_work(a) > item_work(b); });
     std::swap(p.prefill, pre);
+    p.tiles_per_block = 1;
   } else {
-    xcd_order(pre, pre_key, &p.prefill);
+    // tiles per workgroup: pairs in ping-pong pay off once tiles are long
+    int tpb = s.tiles_per_block;
+    if (tpb == 0) {
+      int64_t steps = 0;
+      for (const Item &it : pre) steps += item_work(it);
+      tpb = !pre.empty() && steps >= (int64_t)kPairMinSteps * (int64_t)pre.size() ? 2 : 1;
+    }
+    p.tiles_per_block = tpb;
+    xcd_order(pre, pre_key, tpb, &p.prefill);
   }
   std::swap(p.decode, dec);
   p.plan_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_start)

@@ -258,7 +258,7 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
-    mx = fmaxf(mx, shfl_xor(mx, 32)) * c;
+    mx = max_halves(mx) * c;
     if (mx > mref + 8.f) {
       const float al = fast_exp2(mref - mx);  // 0 on the first update
       lrun *= al;
@@ -323,7 +323,7 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
   }
 
   // ---- epilogue: this lane holds channels 32*db + (i/4)*8 + 4*half + i%4 of row m
-  float l = lrun + shfl_xor(lrun, 32);
+  float l = sum_halves(lrun);
   if (!rowv) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (it.split < 0) {

@@ -34,6 +34,12 @@ constexpr int kPrefillKeys = 64;      // keys per LDS tile
 constexpr int kDecodeRows = 16;       // bf16 split-KV item: 16 MFMA columns
 constexpr int kDecodeKeys = 32;       // keys per decode step
 constexpr int kDecodeWavesPerBlock = 4;
+// MFMA tiles per workgroup when the shape leaves it to the planner: pairs
+// (8 wavefronts in ping-pong, prefill_pair.h) when the batch's tiles average at
+// least this many 64-key steps; shorter tiles run one per 4-wavefront
+// workgroup (prefill_tile.h), two workgroups per CU, which hides their
+// fixed per-tile cost better.
+constexpr int kPairMinSteps = 24;
 constexpr int kF32Rows = 16;          // fp32 tile rows
 constexpr int kF32Keys = 32;          // fp32 keys per LDS tile
 constexpr int kNumXcd = 8;            // MI355X: 8 XCDs, blocks go round-robin
@@ -74,6 +80,7 @@ struct HostPlan {
   int32_t cascade_depth = 0;
   int64_t n_partials = 0;
   int32_t n_cascade_items = 0, cascade_members = 0, decode_chunk = 0;
+  int32_t tiles_per_block = 1;     // MFMA tiles per workgroup (1 or 2)
   int32_t n_prefill_real = 0;      // items before padding
   double plan_us = 0;
   PlanScratch tmp;
@@ -86,6 +93,7 @@ struct HostPlan {
     n_partials = 0;
     n_cascade_items = cascade_members = decode_chunk = 0;
     n_prefill_real = 0;
+    tiles_per_block = 1;
     plan_us = 0;
   }
 };
@@ -94,6 +102,7 @@ struct Shape {
   int32_t Hq, Hkv, D, P, log2P, dtype, max_batch, max_pages_per_req;
   int64_t num_pages, max_tokens;
   int32_t decode_max_rows, split_target, split_min_keys, prefix_detect_keys;
+  int32_t tiles_per_block;  // 0: chosen per batch
   int32_t G() const { return Hq / Hkv; }
 };
 
@@ -130,10 +139,10 @@ struct AttnArgs {
 int launch_store_kv(const void *k, const void *v, const int32_t *slots, int64_t T,
                     int64_t row_bytes, int64_t num_slots, void *kpool, void *vpool,
                     void *stream);
-int launch_prefill_bf16(const AttnArgs &a, void *stream);
+int launch_prefill_bf16(const AttnArgs &a, int tiles_per_block, void *stream);
 int launch_decode_bf16(const AttnArgs &a, void *stream);
 // split-KV chunks and MFMA tiles in one grid (chunks first)
-int launch_fused_bf16(const AttnArgs &pre, const AttnArgs &dec, void *stream);
+int launch_fused_bf16(const AttnArgs &pre, const AttnArgs &dec, int tiles_per_block, void *stream);
 int launch_attn_f32(const AttnArgs &a, void *stream);
 int launch_graph_decode_bf16(const AttnArgs &a, const int32_t *seq_lens, int32_t q_len,
                              int32_t chunk, int32_t maxc, int32_t batch, void *stream);

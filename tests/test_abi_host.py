@@ -262,3 +262,29 @@ def test_full_config_plans(rp):
     info = p.info()
     assert info["cascade_members"] == 64 and info["num_cascade_items"] > 0
     assert info["plan_host_us"] < 50_000
+
+
+def test_tiles_per_block_choice_and_pair_layout(rp):
+    """The planner runs MFMA tiles in pairs (two per 8-wavefront workgroup, in
+    ping-pong) when the batch's tiles average at least 24 steps of 64 keys, else
+    one per 4-wavefront workgroup; the shape can force either.  Either layout
+    covers every visible (token, head, key) exactly once, and the list is padded
+    to whole workgroups on all 8 XCDs."""
+    for cid, want in ((2, 1), (4, 2), (5, 2)):
+        spec = synth.full_config(cid)
+        p = make_plan(rp, spec)
+        p.plan_host(spec.cu_q, spec.L, spec.page_table.shape[1], spec.page_table, spec.groups)
+        assert p.info()["tiles_per_block"] == want, cid
+    for cid in (2, 4):
+        spec = synth.small_config(cid)
+        for tpb in (1, 2):
+            p = make_plan(rp, spec, tiles_per_block=tpb)
+            p.plan_host(spec.cu_q, spec.L, spec.page_table.shape[1], spec.page_table, spec.groups)
+            assert p.info()["tiles_per_block"] == tpb
+            assert len(p.items(0)) % (8 * tpb) == 0
+            check_coverage(rp, p, spec)
+    ok, _ = rp.supports(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, dtype=0,
+                        max_batch=4, num_pages=64, max_tokens=64, max_pages_per_req=8,
+                        tiles_per_block=3)
+    assert not ok
+

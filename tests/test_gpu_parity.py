@@ -40,11 +40,17 @@ def check_full(spec, ht=None, groups=None, **plan_kw):
 
 # ---------------------------------------------------------------- small twins
 
+@pytest.mark.parametrize("tpb", [0, 1, 2])
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
-def test_small_config_matches_oracle(cid):
+def test_small_config_matches_oracle(cid, tpb):
+    """tpb: MFMA tiles per workgroup (0: the planner's choice; 1: one tile per
+    4-wavefront workgroup; 2: two tiles in ping-pong per 8-wavefront one)."""
     spec = synth.small_config(cid)
-    err, plan, _, _ = check_full(spec)
-    print(f"{spec.name}: max err {err:.2e} info {plan.info()}")
+    err, plan, _, _ = check_full(spec, tiles_per_block=tpb)
+    info = plan.info()
+    if tpb and spec.dtype == "bf16" and info["num_prefill_items"]:
+        assert info["tiles_per_block"] == tpb
+    print(f"{spec.name}: max err {err:.2e} info {info}")
 
 
 def test_cascade_equals_unsplit():
@@ -322,14 +328,32 @@ def test_binding_rejects_tensors_of_another_shape():
                      spec.scale)
 
 
+@pytest.mark.parametrize("P", [16, 4, 1])
+def test_tile_pairs_of_unequal_lengths(P):
+    """Tiles in ping-pong pairs whose step counts differ (1 to 14 steps, ranges
+    ending mid-step, an odd number of tiles so one pair has an empty partner)
+    equal the oracle, and equal the same batch run one tile per workgroup."""
+    n = [1, 37, 64, 65, 130, 40, 200]
+    L = [1, 37 + 300, 64, 65 + 700, 130 + 64, 40 + 5, 200 + 651]
+    spec = synth.build(f"pairs_p{P}", "bf16", 8, 2, 128, P, n, L, 77, np.random.default_rng(77), 1.2)
+    ht = synth.host_tensors(spec)
+    e2, p2, out2, _ = check_full(spec, ht, tiles_per_block=2)
+    e1, p1, out1, _ = check_full(spec, ht, tiles_per_block=1)
+    assert p2.info()["tiles_per_block"] == 2 and p1.info()["tiles_per_block"] == 1
+    assert float((out1.float() - out2.float()).abs().max()) <= 2e-2
+    print(f"{spec.name}: err pairs {e2:.2e} single {e1:.2e}")
+
+
 # ---------------------------------------------------------------- full size
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
-def test_full_size_sampled_rows(cid):
+@pytest.mark.parametrize("cid,tpb", [(1, 0), (2, 0), (3, 0), (4, 0), (5, 0), (2, 2), (4, 1), (5, 1)])
+def test_full_size_sampled_rows(cid, tpb):
     """The five workloads at their stated sizes, in the launch configuration the
-    benchmark times; sampled requests and rows are checked against the oracle on
-    the sub-problem of exactly the pages they reference; the store is checked
-    bit-exact on those pages."""
+    benchmark times (tpb 0: the planner picks the tiles per workgroup, as in the
+    benchmark), plus the other tile arrangement for the prefill-heavy ones;
+    sampled requests and rows are checked against the oracle on the sub-problem
+    of exactly the pages they reference; the store is checked bit-exact on those
+    pages."""
     spec = synth.full_config(cid)
     rng = np.random.default_rng(cid)
     if cid == 1:
@@ -341,7 +365,9 @@ def test_full_size_sampled_rows(cid):
     sub = H.subproblem(spec, db, reqs)          # taken before the store
     rows = H.pick_rows(spec, reqs, rng)
     sub_rows = rows[sub.token_map]
-    out, plan = H.gpu_forward(spec, db)
+    out, plan = H.gpu_forward(spec, db, tiles_per_block=tpb)
+    if tpb:
+        assert plan.info()["tiles_per_block"] == tpb
     ref, _, kp_ref, vp_ref = oracle.store_then_attend(sub.spec, sub.tensors, rows=sub_rows,
                                                       nthreads=8)
     got = H.to_f64(out[torch.from_numpy(sub.token_map).cuda()])

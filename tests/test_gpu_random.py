@@ -48,6 +48,7 @@ def random_spec(seed):
                        np.random.default_rng(seed), 1.2)
     kw = dict(split_min_keys=int(rng.choice([0, 32, 64, 256])),
               split_target=int(rng.choice([0, 64, 512])))
+    kw["tiles_per_block"] = int(rng.choice([0, 1, 2]))
     return spec, kw
 
 
