@@ -11,8 +11,8 @@
 // Tile layout, masking, softmax and operand formats are those of the 4-wavefront
 // tile (prefill_tile.h); only the schedule differs:
 //   round r, group 0:  G(r) | V(r)          group 1:  V(r-1) | G(r)
-//   G(r): O += P(r-1) V(r-1) from V buffer (r-1)%2, then S(r) from K buffer r%2
-//         (in this order only one of P(r-1) and S(r) is held at a time)
+//   G(r): S(r) from K buffer r%2, then O += P(r-1) V(r-1) from V buffer
+//         (r-1)%2 (S(r) is complete by the time the vector phase reads it)
 //   V(r): loads of K(r+2) into K buffer r%2 and of V(r+1) into V buffer
 //         (r+1)%2; softmax of S(r) into P(r); wait for the loads issued in
 //         V(r-1), which G(r+1) reads; page ids of step r+3.
@@ -165,6 +165,8 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
 #pragma unroll
       for (int i = 0; i < 4; ++i) off[i] = (uint32_t)lane_off[i];
     } else {
+      // (a real branch: the clamped offsets are computed only on this path)
+      asm volatile("");
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         off[i] = (uint32_t)(lane_off[i] + (min(4 * i + drow, jmax) - (4 * i + drow)) * (int32_t)row_bytes);
@@ -220,27 +222,6 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
   // ---- matrix phase of round r
   auto gphase = [&](int r, const unsigned char *Kb, const unsigned char *Vp) {
     if (r > T) return;
-    if (r >= 1) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const unsigned char *rp = Vp + (vrow + 16 * s2 + 32 * kb) * ROWB + 8 * (vq & 1);
-            const v4i16 lo = tr_read(rp + 16 * ((vc0 + 4 * db) ^ vx));
-            const v4i16 hi = tr_read(rp + 8 * ROWB + 16 * ((vc0 + 4 * db) ^ vx ^ 1));
-            const bf16x8 vf = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[db] = mfma32(vf, pf[kb][s2], o[db]);
-          }
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
-        if (blk + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
-      }
-    }
     if (r < T) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -269,6 +250,27 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
       }
       // the products stay in this phase
       asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+    }
+    if (r >= 1) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const unsigned char *rp = Vp + (vrow + 16 * s2 + 32 * kb) * ROWB + 8 * (vq & 1);
+            const v4i16 lo = tr_read(rp + 16 * ((vc0 + 4 * db) ^ vx));
+            const v4i16 hi = tr_read(rp + 8 * ROWB + 16 * ((vc0 + 4 * db) ^ vx ^ 1));
+            const bf16x8 vf = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[db] = mfma32(vf, pf[kb][s2], o[db]);
+          }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+        if (blk + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+      }
     }
   };
 
