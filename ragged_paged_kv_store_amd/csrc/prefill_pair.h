@@ -320,12 +320,14 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
           s[kb][i] = (32 * kb + (i >> 2) * 8 + (i & 3)) <= rel ? s[kb][i] : kNegInf;
     }
     hook(0);
-    float mx = kNegInf;
+    // one 3-input max per two logits, in two independent chains
+    float mx0 = kNegInf, mx1 = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
-    mx = max_halves(mx) * c;
+    for (int i = 0; i < 16; i += 2) {
+      mx0 = fmaxf(fmaxf(mx0, s[0][i]), s[0][i + 1]);
+      mx1 = fmaxf(fmaxf(mx1, s[1][i]), s[1][i + 1]);
+    }
+    float mx = max_halves(fmaxf(mx0, mx1)) * c;
     if (mx > mref + 8.f) {
       const float al = fast_exp2(mref - mx);
       lrun *= al;
@@ -334,7 +336,10 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
       for (int db = 0; db < 4; ++db) o[db] = o[db] * al;
     }
     const float mu = mref == kNegInf ? 0.f : mref;
-    float sum = 0.f;
+    // the row sum adds the bf16 weights the PV product uses, two per
+    // instruction (v_dot2 against (1, 1): exact products, fp32 sums)
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float sum0 = 0.f, sum1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -344,8 +349,10 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
         for (int j = 0; j < 4; ++j) {
           const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * s2 + 2 * j], c, -mu));
           const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * s2 + 2 * j + 1], c, -mu));
-          sum += p0 + p1;
-          w[j] = pack_bf16x2(p0, p1);
+          const bf16x2 pp = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+          float &acc = (j & 1) ? sum1 : sum0;
+          acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
+          w[j] = __builtin_bit_cast(uint32_t, pp);
         }
         pf[kb][s2] = as_bf16x8(w);
         // computed here, not sunk toward its use in the next matrix phase
@@ -353,7 +360,7 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
         asm volatile("" : "+v"(pf[kb][s2]));
         if (2 * kb + s2 < 3) hook(2 * kb + s2 + 1);
       }
-    lrun += sum;
+    lrun += sum0 + sum1;
   };
 
   // ---- vector phase of round r: Kn = K buffer r%2, Vn = V buffer (r+1)%2;
