@@ -103,7 +103,7 @@ typedef struct rpkv_shape {
                                 wavefronts, one tile), 2 (eight wavefronts, two
                                 tiles in ping-pong), 0 (default): 2 when the
                                 batch's tiles average at least 24 key steps of
-                                64, else 1                                      */
+                                64 and pages hold >= 16 keys, else 1            */
 } rpkv_shape;
 
 /* Cascade hint (SGLang source walkthrough "Attention backends", 3.3 "Cascade

@@ -679,8 +679,10 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
     std::swap(p.prefill, pre);
     p.tiles_per_block = 1;
   } else {
-    // tiles per workgroup: pairs in ping-pong pay off once tiles are long
+    // tiles per workgroup: pairs in ping-pong pay off once tiles are long (and
+    // pages hold >= 16 keys: the pair body for smaller pages spills registers)
     int tpb = s.tiles_per_block;
+    if (tpb == 0 && s.P < 16) tpb = 1;
     if (tpb == 0) {
       int64_t steps = 0;
       for (const Item &it : pre) steps += item_work(it);
