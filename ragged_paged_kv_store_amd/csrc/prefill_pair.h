@@ -145,8 +145,6 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
     asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sbase), "{m0}"(lds_addr(buf, i))
                  : "memory");
   };
-  // Loads of step t into `buf`.  With big pages, steps before the range end
-  // address a scalar base plus the fixed 32-bit lane offsets.
   // (big pages) scalar base of this wavefront's 16 rows of step t
   auto step_base = [&](const Ids &d, int t, const char *pool) {
     const int32_t p = clamp_page(__builtin_amdgcn_readfirstlane(d.pg), a.num_pages);
@@ -173,6 +171,9 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
     }
     return pool + (p * page_bytes + (int64_t)(ebs & pmask) * row_bytes);
   };
+  // Loads of step t into `buf`.  With big pages, steps before the range end
+  // address a scalar base plus the fixed 32-bit lane offsets; otherwise per-lane
+  // addresses, rows past the range end reading zeros.
   auto issue = [&](const Ids &d, int t, const char *pool, unsigned char *buf) {
     const int kt = kbeg + t * BN;
     if (BIGPAGE && kt + BN <= kend) {
@@ -208,6 +209,7 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
     issue(i0, 0, kpool, K0);
     issue(i0, 0, vpool, V0);
     if (T > 1) issue(ids[1], 1, kpool, K1);
+    ids[0] = i0;  // (a valid page for the loads past a short tile's end)
     if (T > 2) fetch_ids(ids[0], kbeg + 2 * BN);
     // the Q row goes out beside the first K/V loads, and one wait covers them
     // all: past it the compiler sees no vector load of its own pending (it
@@ -305,8 +307,6 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
     }
   };
 
-  // ---- vector phase of round r: Kn = K buffer r%2, Vn = V buffer (r+1)%2;
-  // P = r%2 (the parity is static in the unrolled loop)
   // softmax of S(r) into P(r); hook(h) runs before the row max (h = 0) and
   // after each of the first three 16-key blocks of exponentials (h = 1..3)
   auto softmax = [&](int r, auto &&hook) {
@@ -364,10 +364,10 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
   };
 
   // ---- vector phase of round r: Kn = K buffer r%2, Vn = V buffer (r+1)%2;
-  // P = r%2 (the parity is static in the unrolled loop).  The 8 loads go out
-  // two at a time between parts of the softmax, so their issue (the address
-  // unit takes a while per 1 KiB load, and four wavefronts issue together)
-  // overlaps the exponentials; near the range end they go out first.
+  // P = r%2 (the parity is static in the unrolled loop).  With big pages the 8
+  // loads go out two at a time between parts of the softmax, so their issue
+  // (the address unit takes a while per 1 KiB load, and four wavefronts issue
+  // together) overlaps the exponentials; with small pages they go out first.
   auto vphase = [&](int r, auto P, unsigned char *Kn, unsigned char *Vn) {
     if (r < 0 || r >= T) return;
     const bool f_ids = r + 3 < T, f_k = r + 2 < T, f_v = r + 1 < T;
