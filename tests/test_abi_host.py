@@ -243,9 +243,13 @@ def test_random_batches_covered_exactly_once(rp, seed):
     dtype = "bf16" if seed % 3 else "f32"
     spec = synth.build("r", dtype, G * Hkv, Hkv, 128, P, n, L, seed, np.random.default_rng(seed), 1.2)
     kw = dict(split_min_keys=int(rng.choice([0, 32, 64])), split_target=int(rng.choice([0, 64])))
+    kw["tiles_per_block"] = int(rng.choice([0, 1, 2]))
     p = make_plan(rp, spec, **kw)
     p.plan_host(spec.cu_q, spec.L, spec.page_table.shape[1], spec.page_table)
     check_coverage(rp, p, spec)
+    if dtype == "bf16" and kw["tiles_per_block"]:
+        assert p.info()["tiles_per_block"] == kw["tiles_per_block"]
+        assert len(p.items(0)) % (8 * kw["tiles_per_block"]) == 0
 
 
 def test_full_config_plans(rp):
