@@ -45,6 +45,24 @@ int main(void) {
   int32_t count = 0;
   rpkv_plan_get_items(plan, 1, NULL, 0, &count);
   printf("decode_list %d\n", count);
+  printf("tiles_per_block %d\n", info.tiles_per_block);
+
+  /* the same batch with the MFMA tiles forced into ping-pong pairs: the field
+   * after prefix_detect_keys reaches the planner and the summary reports it */
+  rpkv_shape sp = s;
+  sp.tiles_per_block = 2;
+  rpkv_plan *pair_plan = NULL;
+  if (rpkv_plan_create(&sp, &pair_plan) != RPKV_OK) return 1;
+  if (rpkv_plan_batch(pair_plan, 4, cu, L, 64, NULL, NULL, 0) != RPKV_OK) return 1;
+  rpkv_plan_info pinfo;
+  if (rpkv_plan_get_info(pair_plan, &pinfo) != RPKV_OK) return 1;
+  int32_t npre = 0;
+  rpkv_plan_get_items(pair_plan, 0, NULL, 0, &npre);
+  printf("pairs %d %d %d\n", pinfo.tiles_per_block, pinfo.num_prefill_items, npre % 16);
+  rpkv_plan_destroy(pair_plan);
+  sp.tiles_per_block = 3;
+  st = rpkv_supports(&sp);
+  printf("tpb_bad %d\n", (int)st);
 
   /* a request with more new tokens than KV length is rejected with a message */
   const int32_t Lbad[4] = {300, 20, 777, 1000};

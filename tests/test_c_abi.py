@@ -38,6 +38,10 @@ def test_header_is_plain_c_and_host_calls_work(report):
     assert int(report["decode_items"]) >= 2 * 8          # two decodes, 8 KV heads
     assert report["last"] == "299 339 340 341"
     assert int(report["decode_list"]) == int(report["decode_items"])
+    assert report["tiles_per_block"] == "1"              # short tiles: one per workgroup
+    tpb, npre, pad = report["pairs"].split()
+    assert tpb == "2" and npre == report["prefill_items"] and pad == "0"
+    assert report["tpb_bad"] == "1"                      # INVALID_ARG
     assert report["plan_bad"] == "1 msg"                 # INVALID_ARG with a message
 
 
