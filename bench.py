@@ -213,6 +213,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="uniform decode batches only: capture the whole step (device metadata "
                          "build + 32 graph-decode forwards) in one HIP graph and time its replays")
+    ap.add_argument("--tiles-per-block", type=int, default=0, choices=[0, 1, 2],
+                    help="MFMA tiles per workgroup (0: the planner's choice, as timed by "
+                         "default; 1: one per 4-wavefront workgroup; 2: ping-pong pairs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -265,7 +268,8 @@ def main():
     pt = layer0.page_table
     sm = layer0.slot_mapping
     # the radix workload's levels are found from the host page table each step
-    plan = H.make_plan(spec, prefix_detect_keys=RADIX_DETECT_KEYS if radix else 0)
+    plan = H.make_plan(spec, prefix_detect_keys=RADIX_DETECT_KEYS if radix else 0,
+                       tiles_per_block=args.tiles_per_block)
     pt_host = spec.page_table if radix else None
 
     def step():
@@ -401,7 +405,9 @@ def main():
                     unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = dom
-    roof["traffic"] = measured_traffic(args.workload, dom) if layers == LAYERS else None
+    # counters were taken on the default run (32 layers, the planner's tile arrangement)
+    roof["traffic"] = (measured_traffic(args.workload, dom)
+                       if layers == LAYERS and args.tiles_per_block == 0 else None)
 
     flat = None
     if radix:
