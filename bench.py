@@ -9,13 +9,17 @@ log-sum-exp merge).  Each layer has its own q/k/v/out and KV pools; pools are
 cycled so the working set between reuses exceeds the 256 MB Infinity Cache.
 Inputs are seeded synthetic tensors already resident in HBM.
 
-Default workload: the Llama-3-8B-shaped mixed layer (Hq=32, Hkv=8, D=128,
-page_size=16; query lens [2000, 512, 1 x 6]; decode histories uniform in
-[512, 4096]); value = algorithmic attention TFLOP/s (unmasked query-key pairs x
-4 x D x Hq) over the whole step.  --workload picks another of the five batches
-(the decode-heavy one reports KV-read GB/s); --workload radix runs 128 decodes
-under a three-level shared-prefix tree whose levels the planner finds from the
-page table each step, and also times the same steps with the levels off.
+Default workload: the shared-prefix cascade batch, the largest of the five
+(Hq=64, Hkv=8, D=128, page_size=16; 64 one-token decodes sharing an 8192-token
+prefix with own tails uniform in [64, 1024], plus 2 chunked prefills of 4096 new
+tokens over 28672 cached); value = algorithmic attention TFLOP/s (unmasked
+query-key pairs x 4 x D x Hq) over the whole step.  The decode-heavy batch
+(256 decodes, KV uniform in [1024, 8192]) is timed after it in the same run and
+reported under extra.decode_heavy as KV-read GB/s with its own HBM roofline.
+--workload picks another batch as the headline (the decode-heavy one reports
+KV-read GB/s); --workload radix runs 128 decodes under a three-level
+shared-prefix tree whose levels the planner finds from the page table each step,
+and also times the same steps with the levels off.
 
 Prints ONE JSON line (rank 0) with the roofline of the dominant kernel, measured
 with HIP events on the launch stream in a second pass over the same steps, and
@@ -38,6 +42,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 LAYERS = 32
+METRIC = "attention TFLOP/s (prefill-heavy) and KV-read GB/s (decode-heavy), 1 MI355X"
 
 WORKLOADS = {
     "c1": (1, "c1_tiny_mixed_fp32: query lens [6,3,1], KV [6,7,9], Hq=4 Hkv=2 D=64 page_size=1, fp32"),
@@ -201,13 +206,264 @@ def cpu_baseline(spec, db, H, budget_flops: float = 40e9):
                 sample=sample + f", fp64, {dt:.2f} s wall", seconds=dt)
 
 
+def setup(spec, layers, torch, H, tiles_per_block=0, prefix_detect_keys=0):
+    """Per-layer device buffers of one workload: q/k/v/out for up to 8 layers and
+    KV pool sets cycled so that more than 2 GB lies between reuses of a pool."""
+    layer0 = H.device_contents(spec, seed=2024)
+    pool_bytes = 2 * layer0.kpool.numel() * layer0.kpool.element_size()
+    npools = int(min(layers, max(2, math.ceil(2e9 / pool_bytes))))
+    pools = [(layer0.kpool, layer0.vpool)]
+    for j in range(1, npools):
+        d = H.device_contents(spec, seed=2024 + j)
+        pools.append((d.kpool, d.vpool))
+        del d
+    qkv = [(layer0.q, layer0.k, layer0.v)]
+    nq = min(layers, 8)
+    for j in range(1, nq):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(77 + j)
+        dt = layer0.q.dtype
+        qkv.append(tuple(torch.randn(t.shape, generator=g, device="cuda").to(dt)
+                         for t in (layer0.q, layer0.k, layer0.v)))
+    outs = [torch.empty_like(layer0.q) for _ in range(nq)]
+    plan = H.make_plan(spec, prefix_detect_keys=prefix_detect_keys,
+                       tiles_per_block=tiles_per_block)
+    return dict(layer0=layer0, pools=pools, npools=npools, qkv=qkv, nq=nq, outs=outs, plan=plan)
+
+
+def progress(msg):
+    """A progress line on stderr (the JSON line alone goes to stdout)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def run_steps(step, steps, warmup, torch):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def roofline_of(dom, times, alg, decode_heavy):
+    """Roofline of the dominant kernel from its HIP-event average duration."""
+    n_l, ms_l = times[dom]
+    avg_s = ms_l / n_l * 1e-3
+    if dom == "fused" and decode_heavy:
+        # decodes only: the launch streams every unique KV byte of the layer
+        # (shared-prefix levels once, tails per request)
+        roof = dict(bound="hbm", achieved=alg["kv_total"] / avg_s / 1e9, peak=PEAK_HBM_GBPS,
+                    unit="GB/s")
+    elif dom in ("prefill", "fused"):
+        # the fused launch also streams the split-KV chunks; only the tiles'
+        # algorithmic FLOPs are credited
+        roof = dict(bound="mfma", achieved=alg["flops_prefill"] / avg_s / 1e12,
+                    peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
+    elif dom == "decode":
+        roof = dict(bound="hbm", achieved=alg["kv_decode"] / avg_s / 1e9, peak=PEAK_HBM_GBPS,
+                    unit="GB/s")
+    elif dom == "store":
+        roof = dict(bound="hbm", achieved=alg["store_bytes"] / avg_s / 1e9, peak=PEAK_HBM_GBPS,
+                    unit="GB/s")
+    else:
+        roof = dict(bound="alu", achieved=alg["flops_total"] / avg_s / 1e12, peak=78.6,
+                    unit="TFLOP/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = dom
+    roof["avg_us"] = avg_s * 1e6
+    return roof
+
+
+def measure(workload, args, torch, rp, H, synth, cpu=True):
+    """Time one workload: `args.steps` steps (prepare_metadata + layers x forward)
+    after `args.warmup` untimed ones, then the same steps again with HIP events
+    around every launch for the per-kernel averages and the roofline."""
+    cid, desc = WORKLOADS[workload]
+    layers = args.layers
+    radix = workload == "radix"
+    spec = synth.radix_tree() if radix else synth.full_config(cid)
+    stream = torch.cuda.current_stream()
+    progress(f"{workload}: drawing inputs")
+    b = setup(spec, layers, torch, H, tiles_per_block=args.tiles_per_block,
+              prefix_detect_keys=RADIX_DETECT_KEYS if radix else 0)
+    progress(f"{workload}: {args.warmup} warm-up + {args.steps} timed steps of {layers} layers")
+    layer0, pools, npools, qkv, nq, outs, plan = (b[k] for k in ("layer0", "pools", "npools",
+                                                                 "qkv", "nq", "outs", "plan"))
+    pt = layer0.page_table
+    sm = layer0.slot_mapping
+    # the radix workload's levels are found from the host page table each step
+    pt_host = spec.page_table if radix else None
+
+    def step():
+        plan.prepare(spec.cu_q, spec.L, pt, pt_host, spec.groups, stream=stream)
+        for l in range(layers):
+            kp, vp = pools[l % npools]
+            q, k, v = qkv[l % nq]
+            plan.forward(q, k, v, sm, kp, vp, outs[l % nq], spec.scale, stream=stream)
+
+    ms_per_step = run_steps(step, args.steps, args.warmup, torch)
+    info = plan.info()
+    progress(f"{workload}: {ms_per_step:.3f} ms per step; per-launch timing pass")
+
+    # second pass over the same steps with HIP events around every launch
+    plan.timing_enable(True, max_launches=8 * layers * args.steps + 64)
+    for _ in range(args.steps):
+        step()
+    times = plan.timing_collect()
+    plan.timing_enable(False)
+    torch.cuda.synchronize()
+
+    alg = algorithmic(spec, plan.cascade_tree())
+    per_kernel = {k: {"launches": n, "avg_us": (ms * 1e3 / n) if n else None}
+                  for k, (n, ms) in times.items()}
+    decode_heavy = alg["all_decode"] and spec.dtype == "bf16"
+    if decode_heavy:
+        value = alg["kv_total"] * layers / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+    else:
+        value = alg["flops_total"] * layers / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+    # dominant kernel: the one with the largest summed time
+    dom = max((k for k in times if times[k][0]), key=lambda k: times[k][1])
+    roof = roofline_of(dom, times, alg, decode_heavy)
+    # counters were taken on the default run (32 layers, the planner's tile arrangement)
+    roof["traffic"] = (measured_traffic(workload, dom)
+                       if layers == LAYERS and args.tiles_per_block == 0 else None)
+
+    flat = None
+    if radix:
+        # the same steps with the levels off: every request streams its whole prefix
+        fplan = H.make_plan(spec)
+
+        def fstep():
+            fplan.prepare(spec.cu_q, spec.L, pt, None, [], stream=stream)
+            for l in range(layers):
+                kp, vp = pools[l % npools]
+                q, k, v = qkv[l % nq]
+                fplan.forward(q, k, v, sm, kp, vp, outs[l % nq], spec.scale, stream=stream)
+        flat_ms = run_steps(fstep, args.steps, args.warmup, torch)
+        flat = {"ms_per_step": round(flat_ms, 4), "speedup_with_levels": round(flat_ms / ms_per_step, 3),
+                "kv_bytes_per_layer": int(algorithmic(spec, [])["kv_total"])}
+
+    meta_us = metadata_build_us(spec, layer0, rp, torch)
+    cpu_line = None
+    if cpu:
+        progress(f"{workload}: fp64 oracle on the host (cpu_baseline)")
+        cpu_line = cpu_baseline(spec, layer0, H)
+        cpu_line.pop("seconds", None)
+        if unit == "GB/s":
+            cpu_line["note"] = "oracle rate in TFLOP/s of the sampled rows"
+    res = dict(
+        desc=desc, spec=spec, value=value, unit=unit, ms_per_step=ms_per_step, roofline=roof,
+        cpu_baseline=cpu_line, npools=npools,
+        extra={
+            "per_kernel": per_kernel,
+            "layer_us": round(ms_per_step * 1e3 / layers, 2),
+            "attention_tflops": round(alg["flops_total"] * layers / (ms_per_step * 1e-3) / 1e12, 3),
+            "kv_read_GBps": round(alg["kv_total"] * layers / (ms_per_step * 1e-3) / 1e9, 1),
+            "decode_kernel_GBps": (round(alg["kv_decode"] / (times["decode"][1] / times["decode"][0]
+                                                             * 1e-3) / 1e9, 1)
+                                   if times["decode"][0] else None),
+            "split_kv_in_fused_launch": bool(times.get("fused", (0, 0))[0]),
+            "algorithmic_per_layer": alg,
+            "plan": info,
+            "metadata_build_us": meta_us,
+            "without_cascade_levels": flat,
+            "cascade_tree": {"levels": info["num_cascade_levels"], "depth": info["cascade_depth"]},
+        })
+    del b, layer0, pools, qkv, outs, plan
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def graph_bench(args, torch, rp, H, synth):
+    """--graph: the whole decode step (device metadata build + layers x
+    graph-decode forward) captured in one HIP graph; its replays are timed."""
+    cid, desc = WORKLOADS[args.workload]
+    layers = args.layers
+    spec = synth.full_config(cid)
+    n0 = int(spec.n[0])
+    if not (np.all(spec.n == n0) and n0 * spec.G <= 16 and spec.dtype == "bf16"):
+        print("bench.py: --graph needs a uniform bf16 decode batch (e.g. --workload c3)",
+              file=sys.stderr)
+        sys.exit(2)
+    b = setup(spec, layers, torch, H)
+    layer0, pools, npools, qkv, nq, outs = (b[k] for k in ("layer0", "pools", "npools", "qkv",
+                                                           "nq", "outs"))
+    pt = layer0.page_table
+    stream = torch.cuda.current_stream()
+    gplan = H.make_plan(spec)
+    max_seq = int(spec.L.max())
+    gplan.graph_decode_init(spec.bs, n0, max_seq)
+    nc_d = torch.from_numpy((spec.L - spec.n).astype(np.int32)).cuda()
+    n_d = torch.from_numpy(spec.n.astype(np.int32)).cuda()
+    meta = {k: torch.empty(sz, dtype=torch.int32, device="cuda") for k, sz in
+            (("query_start_loc", spec.bs + 1), ("seq_lens", spec.bs), ("positions", spec.T),
+             ("slot_mapping", spec.T), ("logits_indices", spec.bs), ("counts", 2))}
+    gstream = torch.cuda.Stream()
+
+    def gstep(st):
+        rp.build_metadata(nc_d, n_d, pt, spec.P, max_tokens=spec.T, out=meta, stream=st)
+        for l in range(layers):
+            kp, vp = pools[l % npools]
+            q, k, v = qkv[l % nq]
+            gplan.graph_decode_forward(spec.bs, q, k, v, meta["slot_mapping"], kp, vp,
+                                       meta["seq_lens"], pt, outs[l % nq], spec.scale,
+                                       stream=st)
+
+    with torch.cuda.stream(gstream):
+        gstep(gstream.cuda_stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gstream):
+        gstep(torch.cuda.current_stream().cuda_stream)
+    graph_ms = run_steps(graph.replay, args.steps, args.warmup, torch)
+    # per-kernel durations of the same launches, eagerly, with HIP events
+    gplan.timing_enable(True, max_launches=4 * layers * args.steps + 64)
+    for _ in range(args.steps):
+        gstep(stream.cuda_stream)
+    gtimes = gplan.timing_collect()
+    gplan.timing_enable(False)
+    torch.cuda.synchronize()
+    alg = algorithmic(spec, [])
+    dec_n, dec_ms = gtimes["decode"]
+    kv_rate = alg["kv_total"] * layers / (graph_ms * 1e-3) / 1e9
+    avg_s = dec_ms / dec_n * 1e-3
+    line = {
+        "metric": METRIC,
+        "value": round(kv_rate, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(graph_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
+        "data": "synthetic (seeded N(0,1) tensors, seeded page allocation)",
+        "config": {"workload": desc, "layers_per_step": layers, "pool_sets": npools,
+                   "batch": spec.bs, "tokens": spec.T,
+                   "step": f"one HIP graph: device metadata build + {layers} x graph-decode "
+                           "forward (store_kv + split-KV + merge)"},
+        "roofline": {"bound": "hbm", "achieved": alg["kv_decode"] / avg_s / 1e9,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": alg["kv_decode"] / avg_s / 1e9 / PEAK_HBM_GBPS,
+                     "kernel": "graph decode", "traffic": None},
+        "cpu_baseline": None,
+        "extra": {"per_kernel": {k: {"launches": nn, "avg_us": (ms * 1e3 / nn) if nn else None}
+                                 for k, (nn, ms) in gtimes.items()},
+                  "layer_us": round(graph_ms * 1e3 / layers, 2)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS),
+                    help="headline workload (default c5, the largest single-GPU batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-heavy", action="store_true",
+                    help="skip the decode-heavy batch (c3) timed after the headline workload")
     ap.add_argument("--layers", type=int, default=LAYERS,
                     help="layers per step (a model has 32; fewer only for short profiling runs)")
     ap.add_argument("--graph", action="store_true",
@@ -241,237 +497,42 @@ def main():
     from tests import gpu_harness as H
     from workloads import synth
 
-    cid, desc = WORKLOADS[args.workload]
-    layers = args.layers
-    radix = args.workload == "radix"
-    spec = synth.radix_tree() if radix else synth.full_config(cid)
-    stream = torch.cuda.current_stream()
-
-    # per-layer buffers: q/k/v/out per layer, pools cycled over npools sets
-    layer0 = H.device_contents(spec, seed=2024)
-    pool_bytes = 2 * layer0.kpool.numel() * layer0.kpool.element_size()
-    npools = int(min(layers, max(2, math.ceil(2e9 / pool_bytes))))
-    pools = [(layer0.kpool, layer0.vpool)]
-    for j in range(1, npools):
-        d = H.device_contents(spec, seed=2024 + j)
-        pools.append((d.kpool, d.vpool))
-        del d
-    qkv = [(layer0.q, layer0.k, layer0.v)]
-    nq = min(layers, 8)
-    for j in range(1, nq):
-        g = torch.Generator(device="cuda")
-        g.manual_seed(77 + j)
-        dt = layer0.q.dtype
-        qkv.append(tuple(torch.randn(t.shape, generator=g, device="cuda").to(dt)
-                         for t in (layer0.q, layer0.k, layer0.v)))
-    outs = [torch.empty_like(layer0.q) for _ in range(nq)]
-    pt = layer0.page_table
-    sm = layer0.slot_mapping
-    # the radix workload's levels are found from the host page table each step
-    plan = H.make_plan(spec, prefix_detect_keys=RADIX_DETECT_KEYS if radix else 0,
-                       tiles_per_block=args.tiles_per_block)
-    pt_host = spec.page_table if radix else None
-
-    def step():
-        plan.prepare(spec.cu_q, spec.L, pt, pt_host, spec.groups, stream=stream)
-        for l in range(layers):
-            kp, vp = pools[l % npools]
-            q, k, v = qkv[l % nq]
-            plan.forward(q, k, v, sm, kp, vp, outs[l % nq], spec.scale, stream=stream)
-
     if args.graph:
-        n0 = int(spec.n[0])
-        if not (np.all(spec.n == n0) and n0 * spec.G <= 16 and spec.dtype == "bf16"):
-            print("bench.py: --graph needs a uniform bf16 decode batch (e.g. --workload c3)",
-                  file=sys.stderr)
-            sys.exit(2)
-        gplan = H.make_plan(spec)
-        max_seq = int(spec.L.max())
-        gplan.graph_decode_init(spec.bs, n0, max_seq)
-        nc_d = torch.from_numpy((spec.L - spec.n).astype(np.int32)).cuda()
-        n_d = torch.from_numpy(spec.n.astype(np.int32)).cuda()
-        meta = {k: torch.empty(sz, dtype=torch.int32, device="cuda") for k, sz in
-                (("query_start_loc", spec.bs + 1), ("seq_lens", spec.bs), ("positions", spec.T),
-                 ("slot_mapping", spec.T), ("logits_indices", spec.bs), ("counts", 2))}
-        gstream = torch.cuda.Stream()
-
-        def gstep(st):
-            rp.build_metadata(nc_d, n_d, pt, spec.P, max_tokens=spec.T, out=meta, stream=st)
-            for l in range(layers):
-                kp, vp = pools[l % npools]
-                q, k, v = qkv[l % nq]
-                gplan.graph_decode_forward(spec.bs, q, k, v, meta["slot_mapping"], kp, vp,
-                                           meta["seq_lens"], pt, outs[l % nq], spec.scale,
-                                           stream=st)
-
-        with torch.cuda.stream(gstream):
-            gstep(gstream.cuda_stream)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=gstream):
-            gstep(torch.cuda.current_stream().cuda_stream)
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        # per-kernel durations of the same launches, eagerly, with HIP events
-        gplan.timing_enable(True, max_launches=4 * layers * args.steps + 64)
-        for _ in range(args.steps):
-            gstep(stream.cuda_stream)
-        gtimes = gplan.timing_collect()
-        gplan.timing_enable(False)
-        torch.cuda.synchronize()
-        alg = algorithmic(spec, [])
-        dec_n, dec_ms = gtimes["decode"]
-        kv_rate = alg["kv_total"] * layers / (graph_ms * 1e-3) / 1e9
-        avg_s = dec_ms / dec_n * 1e-3
-        line = {
-            "metric": "attention TFLOP/s (prefill-heavy) and KV-read GB/s (decode-heavy), 1 MI355X",
-            "value": round(kv_rate, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": round(graph_ms, 4), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
-            "data": "synthetic (seeded N(0,1) tensors, seeded page allocation)",
-            "config": {"workload": desc, "layers_per_step": layers, "pool_sets": npools,
-                       "batch": spec.bs, "tokens": spec.T,
-                       "step": f"one HIP graph: device metadata build + {layers} x graph-decode "
-                               "forward (store_kv + split-KV + merge)"},
-            "roofline": {"bound": "hbm", "achieved": alg["kv_decode"] / avg_s / 1e9,
-                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                         "frac": alg["kv_decode"] / avg_s / 1e9 / PEAK_HBM_GBPS,
-                         "kernel": "graph decode", "traffic": None},
-            "cpu_baseline": None,
-            "extra": {"per_kernel": {k: {"launches": nn, "avg_us": (ms * 1e3 / nn) if nn else None}
-                                     for k, (nn, ms) in gtimes.items()},
-                      "layer_us": round(graph_ms * 1e3 / layers, 2)},
-        }
-        print(json.dumps(line), flush=True)
+        graph_bench(args, torch, rp, H, synth)
         return
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    info = plan.info()
-
-    # second pass over the same steps with HIP events around every launch
-    plan.timing_enable(True, max_launches=8 * layers * args.steps + 64)
-    for _ in range(args.steps):
-        step()
-    times = plan.timing_collect()
-    plan.timing_enable(False)
-    torch.cuda.synchronize()
-
-    alg = algorithmic(spec, plan.cascade_tree())
-    per_kernel = {k: {"launches": n, "avg_us": (ms * 1e3 / n) if n else None}
-                  for k, (n, ms) in times.items()}
-    decode_heavy = alg["all_decode"] and spec.dtype == "bf16"
-    if decode_heavy:
-        metric_value = alg["kv_total"] * layers / (ms_per_step * 1e-3) / 1e9
-        unit = "GB/s"
-    else:
-        metric_value = alg["flops_total"] * layers / (ms_per_step * 1e-3) / 1e12
-        unit = "TFLOP/s"
-    # dominant kernel: the one with the largest summed time
-    dom = max((k for k in times if times[k][0]), key=lambda k: times[k][1])
-    n_l, ms_l = times[dom]
-    avg_s = ms_l / n_l * 1e-3
-    if dom == "fused" and decode_heavy:
-        # decodes only: the launch streams every unique KV byte of the layer
-        # (shared-prefix levels once, tails per request)
-        roof = dict(bound="hbm", achieved=alg["kv_total"] / avg_s / 1e9, peak=PEAK_HBM_GBPS,
-                    unit="GB/s")
-    elif dom in ("prefill", "fused"):
-        # the fused launch also streams the split-KV chunks; only the tiles'
-        # algorithmic FLOPs are credited
-        roof = dict(bound="mfma", achieved=alg["flops_prefill"] / avg_s / 1e12,
-                    peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
-    elif dom == "decode":
-        roof = dict(bound="hbm", achieved=alg["kv_decode"] / avg_s / 1e9, peak=PEAK_HBM_GBPS,
-                    unit="GB/s")
-    elif dom == "store":
-        roof = dict(bound="hbm", achieved=alg["store_bytes"] / avg_s / 1e9, peak=PEAK_HBM_GBPS,
-                    unit="GB/s")
-    else:
-        roof = dict(bound="alu", achieved=alg["flops_total"] / avg_s / 1e12, peak=78.6,
-                    unit="TFLOP/s")
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = dom
-    # counters were taken on the default run (32 layers, the planner's tile arrangement)
-    roof["traffic"] = (measured_traffic(args.workload, dom)
-                       if layers == LAYERS and args.tiles_per_block == 0 else None)
-
-    flat = None
-    if radix:
-        # the same steps with the levels off: every request streams its whole prefix
-        fplan = H.make_plan(spec)
-
-        def fstep():
-            fplan.prepare(spec.cu_q, spec.L, pt, None, [], stream=stream)
-            for l in range(layers):
-                kp, vp = pools[l % npools]
-                q, k, v = qkv[l % nq]
-                fplan.forward(q, k, v, sm, kp, vp, outs[l % nq], spec.scale, stream=stream)
-        for _ in range(args.warmup):
-            fstep()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            fstep()
-        torch.cuda.synchronize()
-        flat_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        flat = {"ms_per_step": round(flat_ms, 4), "speedup_with_levels": round(flat_ms / ms_per_step, 3),
-                "kv_bytes_per_layer": int(algorithmic(spec, [])["kv_total"])}
-
-    meta_us = metadata_build_us(spec, layer0, rp, torch)
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(spec, layer0, H)
-        cpu.pop("seconds", None)
-        if unit == "GB/s":
-            cpu["note"] = "oracle rate in TFLOP/s of the sampled rows"
-
+    r = measure(args.workload, args, torch, rp, H, synth, cpu=not args.no_cpu_baseline)
+    spec = r["spec"]
+    extra = r["extra"]
+    # the decode-heavy batch in the same run: KV-read GB/s against the HBM roofline
+    if args.workload != "c3" and not args.no_decode_heavy:
+        d = measure("c3", args, torch, rp, H, synth, cpu=False)
+        extra["decode_heavy"] = {
+            "workload": d["desc"], "value": round(d["value"], 3), "unit": d["unit"],
+            "ms_per_step": round(d["ms_per_step"], 4), "steps": args.steps,
+            "warmup": args.warmup, "roofline": d["roofline"],
+            "per_kernel": d["extra"]["per_kernel"], "layer_us": d["extra"]["layer_us"],
+            "plan": d["extra"]["plan"],
+        }
     line = {
-        "metric": "attention TFLOP/s (prefill-heavy) and KV-read GB/s (decode-heavy), 1 MI355X",
-        "value": round(metric_value, 3),
-        "unit": unit,
+        "metric": METRIC,
+        "value": round(r["value"], 3),
+        "unit": r["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": spec.dtype,
         "data": "synthetic (seeded N(0,1) tensors, seeded page allocation)",
-        "config": {"workload": desc, "layers_per_step": layers, "pool_sets": npools,
-                   "batch": spec.bs, "tokens": spec.T,
-                   "step": f"prepare_metadata + {layers} x (store_kv + attend)"},
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "extra": {
-            "per_kernel": per_kernel,
-            "layer_us": round(ms_per_step * 1e3 / layers, 2),
-            "attention_tflops": round(alg["flops_total"] * layers / (ms_per_step * 1e-3) / 1e12, 3),
-            "kv_read_GBps": round(alg["kv_total"] * layers / (ms_per_step * 1e-3) / 1e9, 1),
-            "decode_kernel_GBps": (round(alg["kv_decode"] / (times["decode"][1] / times["decode"][0]
-                                                             * 1e-3) / 1e9, 1)
-                                   if times["decode"][0] else None),
-            "split_kv_in_fused_launch": bool(times.get("fused", (0, 0))[0]),
-            "algorithmic_per_layer": alg,
-            "plan": info,
-            "metadata_build_us": meta_us,
-            "without_cascade_levels": flat,
-            "cascade_tree": {"levels": info["num_cascade_levels"], "depth": info["cascade_depth"]},
-        },
+        "config": {"workload": r["desc"], "layers_per_step": args.layers,
+                   "pool_sets": r["npools"], "batch": spec.bs, "tokens": spec.T,
+                   "step": f"prepare_metadata + {args.layers} x (store_kv + attend)"},
+        "roofline": r["roofline"],
+        "cpu_baseline": r["cpu_baseline"],
+        "extra": extra,
     }
     print(json.dumps(line), flush=True)
 

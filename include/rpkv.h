@@ -79,7 +79,8 @@ typedef enum rpkv_dtype {
  * Zero in a tuning field selects the library default. */
 typedef struct rpkv_shape {
   int32_t num_q_heads;       /* Hq                                              */
-  int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0 and Hq / Hkv <= 128          */
+  int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0; Hq / Hkv <= 128 (bf16) or
+                                <= 16 (f32)                                     */
   int32_t head_dim;          /* D: 128 (bf16); 64 or 128 (f32)                  */
   int32_t page_size;         /* tokens per page: a power of two in [1, 1024]    */
   int32_t dtype;             /* rpkv_dtype of q, k, v, the pools and out        */
@@ -104,6 +105,11 @@ typedef struct rpkv_shape {
                                 tiles in ping-pong), 0 (default): 2 when the
                                 batch's tiles average at least 24 key steps of
                                 64 and pages hold >= 16 keys, else 1            */
+  int32_t check_slots;       /* debug: when nonzero, rpkv_store_kv and
+                                rpkv_forward copy slot_mapping to the host
+                                (blocking the host on the stream) and reject
+                                duplicate or out-of-range slots before
+                                enqueueing anything (0: off)                    */
 } rpkv_shape;
 
 /* Cascade hint (SGLang source walkthrough "Attention backends", 3.3 "Cascade
@@ -147,6 +153,12 @@ typedef struct rpkv_plan_info {
   int32_t cascade_depth;       /* longest chain of nested levels          */
   int32_t num_cascade_level_members; /* sum of the levels' member counts  */
   int32_t tiles_per_block;     /* MFMA tiles per workgroup this batch     */
+  int64_t metadata_bytes;      /* device copy of this batch's partition   */
+  int64_t metadata_capacity_bytes; /* the plan's fixed metadata buffer:
+                                  every batch within the capacities fits */
+  int64_t buffer_allocations;  /* device and pinned allocations the plan's
+                                  prepare calls have made (all at the
+                                  first; graph decode's are not counted) */
 } rpkv_plan_info;
 
 /* Kernel timing (benchmarks): per kernel kind, launches and summed durations
@@ -182,9 +194,17 @@ const char *rpkv_last_error(void);
  * shape, else RPKV_ERR_UNSUPPORTED or RPKV_ERR_INVALID_ARG.  No device work. */
 rpkv_status rpkv_supports(const rpkv_shape *shape);
 
-/* Create a plan for one layer type.  Host-only: allocates host memory; device
- * buffers are allocated by the first rpkv_prepare_metadata.  *out receives the
- * plan, owned by the library until rpkv_plan_destroy. */
+/* Create a plan for one layer type (mini-sglang "The attention backend and a
+ * reference implementation", "The interface": a backend is built once for the
+ * model's head shape and KV pool; SGLang source walkthrough "Attention
+ * backends", 3.1: fixed-size metadata buffers allocated ahead of the batches).
+ * Host-only: allocates host memory and fixes the metadata capacity, an upper
+ * bound of the work partition of any batch within the shape's capacities
+ * (max_batch, max_tokens, max_pages_per_req; rpkv_plan_info reports it).  The
+ * device buffers of that capacity (plus a [max_batch, max_pages_per_req] int32
+ * table for CSR page tables) and two pinned staging buffers are allocated once
+ * by the first prepare; no later prepare allocates or frees memory.  *out
+ * receives the plan, owned by the library until rpkv_plan_destroy. */
 rpkv_status rpkv_plan_create(const rpkv_shape *shape, rpkv_plan **out);
 
 /* Release a plan and its device buffers (waits for the device). NULL is a no-op. */
@@ -227,7 +247,14 @@ rpkv_status rpkv_plan_batch(rpkv_plan *plan, int32_t batch, const int32_t *cu_se
  *                      rpkv_workspace_bytes reports the size to provide.
  * The host arrays may be reused by the caller as soon as the call returns.
  * Page ids outside [0, num_pages) that reach a kernel are clamped (results
- * unspecified, no out-of-bounds access). */
+ * unspecified, no out-of-bounds access).
+ * Streams: the work partition is uploaded on `stream` into one plan-owned
+ * device buffer that every batch reuses.  This batch's attend/forward calls must
+ * be ordered after this call on the device (the same stream, or one that waits
+ * on it), and the next prepare on the plan must be ordered after the last of
+ * them; one stream for all of a plan's calls satisfies both.  The host-side
+ * staging is double-buffered: the call blocks only if the upload two batches
+ * back has not finished. */
 rpkv_status rpkv_prepare_metadata(rpkv_plan *plan, int32_t batch, const int32_t *cu_seqlens_q_host,
                                   const int32_t *cache_seqlens_host, const int32_t *page_table_dev,
                                   int64_t page_table_stride, int32_t page_table_cols,
@@ -307,11 +334,16 @@ rpkv_status rpkv_plan_get_cascade_tree(const rpkv_plan *plan, int32_t max_levels
 
 /* ---------------------------------------------------------- once per layer */
 
-/* store_kv / do_kv_cache_update: for t < num_tokens, K pool row slot_mapping[t]
- * = k[t] and V pool row slot_mapping[t] = v[t], bit for bit.  A negative slot
- * is a padding token and writes nothing; a slot >= num_pages*page_size is
- * skipped (never written).  Slots must be distinct (duplicates race).  Uses only
- * the plan's shape; does not need a prepared batch.
+/* store_kv / do_kv_cache_update (mini-sglang "The interface": forward writes
+ * this step's K/V into the pool before attending; vLLM "Attention backends",
+ * Step 2: the cache update scatters new rows by slot_mapping): for t <
+ * num_tokens, K pool row slot_mapping[t] = k[t] and V pool row slot_mapping[t]
+ * = v[t], bit for bit.  A negative slot is a padding token and writes nothing; a
+ * slot >= num_pages*page_size is skipped (never written).  Slots must be
+ * distinct: duplicates race (which row lands is unspecified).  With the shape's
+ * check_slots set, duplicates and out-of-range slots are rejected with
+ * INVALID_ARG before anything is enqueued (see rpkv_check_slot_mapping).  Uses
+ * only the plan's shape; does not need a prepared batch.
  *   k, v          device [num_tokens, Hkv, D]
  *   slot_mapping  device int32 [num_tokens]
  *   k_pool/v_pool device [num_pages*page_size, Hkv, D] of one layer */
@@ -319,7 +351,21 @@ rpkv_status rpkv_store_kv(rpkv_plan *plan, const void *k, const void *v,
                           const int32_t *slot_mapping, int64_t num_tokens, void *k_pool,
                           void *v_pool, void *stream);
 
-/* attend: out[t, h, :] = softmax over the visible keys of request i(t) of
+/* Host-side check of a slot_mapping (the store is a scatter by slot, vLLM
+ * "Attention backends", Step 2: two tokens naming one slot race): INVALID_ARG,
+ * naming the first offending token, if a slot is >= num_pages*page_size or
+ * equals an earlier token's slot; negative slots (padding) are ignored.  No
+ * device work; usable without a GPU.  slots_host [num_tokens] host int32. */
+rpkv_status rpkv_check_slot_mapping(const rpkv_plan *plan, const int32_t *slots_host,
+                                    int64_t num_tokens);
+
+/* attend (mini-sglang "The attention backend and a reference implementation",
+ * "Variable-length, paged attention with prefixes": each request's packed
+ * queries attend its first cache_seqlens[i] pool slots through its page-table
+ * row, bottom-right causal mask, query head h reading KV head h / (Hq / Hkv);
+ * SGLang source walkthrough "Attention backends", 3.3 and 6: decode work split
+ * over key chunks and shared prefixes merged by log-sum-exp):
+ * out[t, h, :] = softmax over the visible keys of request i(t) of
  * scale * <q[t,h,:], K[.]> applied to V, for every token of the prepared batch.
  * Must be enqueued after this layer's store_kv (same stream order).
  *   q     device [T, Hq, D];  out device [T, Hq, D], caller-allocated, must not
@@ -327,9 +373,11 @@ rpkv_status rpkv_store_kv(rpkv_plan *plan, const void *k, const void *v,
 rpkv_status rpkv_attend(rpkv_plan *plan, const void *q, const void *k_pool, const void *v_pool,
                         void *out, float scale, void *stream);
 
-/* forward(q, k, v, layer): rpkv_store_kv of the batch's T tokens, then
- * rpkv_attend, on one stream (write first, then read).  The layer is chosen by
- * the pool pointers passed. */
+/* forward(q, k, v, layer) (mini-sglang "The interface": one call per layer
+ * that writes the step's K/V and then attends, the metadata prepared once per
+ * batch): rpkv_store_kv of the batch's T tokens, then rpkv_attend, on one
+ * stream (write first, then read).  The layer is chosen by the pool pointers
+ * passed. */
 rpkv_status rpkv_forward(rpkv_plan *plan, const void *q, const void *k, const void *v,
                          const int32_t *slot_mapping, void *k_pool, void *v_pool, void *out,
                          float scale, void *stream);
@@ -359,7 +407,8 @@ rpkv_status rpkv_graph_decode_init(rpkv_plan *plan, int32_t max_batch, int32_t q
  * chunks merged by log-sum-exp), on `stream`.  No host synchronisation, no
  * allocation, grids fixed by `batch`: capturable.
  *   seq_lens    device int32 [batch]: q_len <= L_i <= max_seq_len (a request with
- *               L_i < q_len is skipped; keys past max_seq_len are ignored)
+ *               L_i outside that range is skipped: no key is read and its
+ *               output rows are not written)
  *   page_table  device int32 [batch, pt_stride], pt_cols >= ceil(max_seq_len / P)
  *               valid columns
  *   q, out      device [batch*q_len, Hq, D]; k, v [batch*q_len, Hkv, D];

@@ -35,6 +35,7 @@ EXPORTS = (
     "rpkv_store_kv", "rpkv_attend", "rpkv_forward", "rpkv_timing_enable", "rpkv_timing_collect",
     "rpkv_build_metadata", "rpkv_graph_decode_init", "rpkv_graph_decode_forward",
     "rpkv_prepare_metadata_csr", "rpkv_rewrite_block_table", "rpkv_plan_get_cascade_tree",
+    "rpkv_check_slot_mapping",
 )
 
 
@@ -51,7 +52,8 @@ class Shape(ctypes.Structure):
                 ("num_pages", ctypes.c_int64), ("max_tokens", ctypes.c_int64),
                 ("max_pages_per_req", ctypes.c_int32), ("decode_max_rows", ctypes.c_int32),
                 ("split_target", ctypes.c_int32), ("split_min_keys", ctypes.c_int32),
-                ("prefix_detect_keys", ctypes.c_int32), ("tiles_per_block", ctypes.c_int32)]
+                ("prefix_detect_keys", ctypes.c_int32), ("tiles_per_block", ctypes.c_int32),
+                ("check_slots", ctypes.c_int32)]
 
 
 class PrefixGroup(ctypes.Structure):
@@ -68,7 +70,8 @@ class PlanInfo(ctypes.Structure):
                 ("decode_chunk", ctypes.c_int32), ("cascade_members", ctypes.c_int32),
                 ("plan_host_us", ctypes.c_double), ("num_cascade_levels", ctypes.c_int32),
                 ("cascade_depth", ctypes.c_int32), ("num_cascade_level_members", ctypes.c_int32),
-                ("tiles_per_block", ctypes.c_int32)]
+                ("tiles_per_block", ctypes.c_int32), ("metadata_bytes", ctypes.c_int64),
+                ("metadata_capacity_bytes", ctypes.c_int64), ("buffer_allocations", ctypes.c_int64)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -110,6 +113,7 @@ def _load():
         "rpkv_rewrite_block_table": (i32, [i32, vp, i64, i32, i32, vp, i64, vp]),
         "rpkv_graph_decode_forward": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp,
                                             ctypes.c_float, vp]),
+        "rpkv_check_slot_mapping": (i32, [vp, vp, i64]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(L, name)
@@ -207,10 +211,11 @@ def supports(**kw) -> Tuple[bool, str]:
 def make_shape(num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int, dtype: int,
                max_batch: int, num_pages: int, max_tokens: int, max_pages_per_req: int,
                decode_max_rows: int = 0, split_target: int = 0, split_min_keys: int = 0,
-               prefix_detect_keys: int = 0, tiles_per_block: int = 0) -> Shape:
+               prefix_detect_keys: int = 0, tiles_per_block: int = 0,
+               check_slots: int = 0) -> Shape:
     return Shape(num_q_heads, num_kv_heads, head_dim, page_size, dtype, max_batch, num_pages,
                  max_tokens, max_pages_per_req, decode_max_rows, split_target, split_min_keys,
-                 prefix_detect_keys, tiles_per_block)
+                 prefix_detect_keys, tiles_per_block, check_slots)
 
 
 class Plan:
@@ -407,6 +412,12 @@ class Plan:
         out = np.zeros(max(self.batch, 1), np.int32)
         _check(lib.rpkv_last_indices(self._h, out.ctypes.data))
         return out[:self.batch]
+
+    def check_slot_mapping(self, slots_host) -> None:
+        """rpkv_check_slot_mapping on a host array: raises RpkvError
+        (INVALID_ARG) on a duplicate or out-of-range slot."""
+        s = _i32(slots_host).reshape(-1)
+        _check(lib.rpkv_check_slot_mapping(self._h, s.ctypes.data if s.size else None, s.size))
 
     def workspace_bytes(self) -> int:
         need = ctypes.c_size_t()

@@ -36,16 +36,16 @@ struct rpkv_plan {
   bool planned = false;
   bool prepared = false;
   int device = -1;
-  // device copy of the work partition
+  // device copy of the work partition, sized once for the shape's capacities
+  // (rpkv::meta_caps) at the first prepare; every batch's copy fits in it
   char *dmeta = nullptr;
-  size_t dmeta_cap = 0;
-  size_t off_pre = 0, off_dec = 0, off_pbase = 0, off_merge = 0, off_tok = 0, off_indptr = 0,
-         meta_bytes = 0;
+  size_t meta_cap = 0;        // bytes of dmeta and of each staging buffer
+  rpkv::MetaLayout lay{};     // the planned batch's layout
+  int64_t n_alloc = 0;        // allocations made by ensure_device
   // dense copy of a CSR page table (plan-owned, [max_batch, max_pages_per_req])
   int32_t *csr_table = nullptr;
   // pinned staging, two buffers so a new batch never overwrites one in flight
   char *hmeta[2] = {nullptr, nullptr};
-  size_t hmeta_cap[2] = {0, 0};
   hipEvent_t hev[2] = {nullptr, nullptr};
   bool hev_live[2] = {false, false};
   int hcur = 0;
@@ -61,6 +61,9 @@ struct rpkv_plan {
   std::vector<hipEvent_t> ev;
   std::vector<int32_t> ev_kind;
   int32_t n_rec = 0;
+  // host copy of a slot_mapping for the check_slots debug mode
+  std::vector<int32_t> slots_host;
+  std::vector<int64_t> slots_key;
   // graph-capturable decode: fixed capacities and plan-owned partials
   int32_t g_max_batch = 0, g_q_len = 0, g_chunk = 0, g_maxc = 0, g_max_seq = 0;
   float *g_opart = nullptr;
@@ -74,6 +77,22 @@ size_t workspace_need(const rpkv_plan *p) {
   if (p->hp.n_partials == 0) return 0;
   const size_t rows = (size_t)p->hp.n_partials * p->s.Hq;
   return align256(rows * p->s.D * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+// Frees the plan's metadata buffers (the caller has waited for the device).
+void release_device(rpkv_plan *p) {
+  if (p->dmeta) (void)hipFree(p->dmeta);
+  if (p->csr_table) (void)hipFree(p->csr_table);
+  p->dmeta = nullptr;
+  p->csr_table = nullptr;
+  for (int i = 0; i < 2; ++i) {
+    if (p->hmeta[i]) (void)hipHostFree(p->hmeta[i]);
+    if (p->hev[i]) (void)hipEventDestroy(p->hev[i]);
+    p->hmeta[i] = nullptr;
+    p->hev[i] = nullptr;
+    p->hev_live[i] = false;
+  }
+  p->device = -1;
 }
 
 template <class F>
@@ -130,6 +149,7 @@ rpkv_status rpkv_plan_create(const rpkv_shape *shape, rpkv_plan **out) {
   rpkv_plan *p = new (std::nothrow) rpkv_plan();
   if (!p) return fail(RPKV_ERR_CAPACITY, "host allocation failed");
   p->s = s;
+  p->meta_cap = rpkv::meta_layout(rpkv::meta_caps(s)).bytes;
   *out = p;
   return RPKV_OK;
 }
@@ -141,13 +161,8 @@ void rpkv_plan_destroy(rpkv_plan *p) {
     else if (p->g_device >= 0) (void)hipSetDevice(p->g_device);
     (void)hipDeviceSynchronize();
   }
-  if (p->dmeta) (void)hipFree(p->dmeta);
-  if (p->csr_table) (void)hipFree(p->csr_table);
+  release_device(p);
   if (p->g_opart) (void)hipFree(p->g_opart);
-  for (int i = 0; i < 2; ++i) {
-    if (p->hmeta[i]) (void)hipHostFree(p->hmeta[i]);
-    if (p->hev[i]) (void)hipEventDestroy(p->hev[i]);
-  }
   for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
   delete p;
 }
@@ -167,13 +182,54 @@ rpkv_status rpkv_plan_batch(rpkv_plan *p, int32_t batch, const int32_t *cu, cons
     return fail(RPKV_ERR_CAPACITY, "host allocation failed while planning");
   }
   if (st != RPKV_OK) return fail(st, msg);
+  const rpkv::MetaLayout lay = rpkv::meta_layout(rpkv::meta_counts(p->hp_next, p->s.max_batch));
+  if (lay.bytes > p->meta_cap)  // the bound of meta_caps is exceeded: a planner bug
+    return fail(RPKV_ERR_CAPACITY, "work partition of " + std::to_string(lay.bytes) +
+                                       " bytes exceeds the plan's metadata capacity of " +
+                                       std::to_string(p->meta_cap));
   std::swap(p->hp, p->hp_next);
+  p->lay = lay;
   p->planned = true;
   p->ws_need = workspace_need(p);
   return RPKV_OK;
 }
 
 namespace {
+
+// The plan's device buffers and pinned staging, allocated once on the device of
+// the first prepare, at the capacity every batch fits in: the per-batch path
+// never allocates, frees or synchronises the device for memory.
+rpkv_status ensure_device(rpkv_plan *p) {
+  int dev = 0;
+  int e = hipGetDevice(&dev);
+  if (e) return hip_fail(e, "hipGetDevice");
+  if (p->device >= 0) {
+    if (p->device != dev)
+      return fail(RPKV_ERR_INVALID_ARG, "a plan is bound to the device of its first prepare");
+    return RPKV_OK;
+  }
+  const size_t csr_bytes =
+      std::max<size_t>(1, (size_t)p->s.max_batch * p->s.max_pages_per_req) * sizeof(int32_t);
+  const char *what = nullptr;
+  if ((e = hipMalloc((void **)&p->dmeta, p->meta_cap))) what = "hipMalloc (plan metadata)";
+  else if ((e = hipMalloc((void **)&p->csr_table, csr_bytes)))
+    what = "hipMalloc (dense copy of a CSR page table)";
+  else p->n_alloc += 2;
+  for (int i = 0; !what && i < 2; ++i) {
+    if ((e = hipHostMalloc((void **)&p->hmeta[i], p->meta_cap, hipHostMallocDefault)))
+      what = "hipHostMalloc (metadata staging)";
+    else if ((e = hipEventCreateWithFlags(&p->hev[i], hipEventDisableTiming)))
+      what = "hipEventCreate";
+    else ++p->n_alloc;
+  }
+  if (what) {
+    const rpkv_status st = hip_fail(e, what);
+    release_device(p);
+    return st;
+  }
+  p->device = dev;
+  return RPKV_OK;
+}
 
 // prepare_metadata; csr_indptr (a CSR page table's row offsets) rides along in
 // the metadata upload
@@ -202,80 +258,34 @@ rpkv_status prepare_impl(rpkv_plan *p, int32_t batch, const int32_t *cu, const i
                       std::to_string(ws ? ws_bytes : 0) + " given");
     if ((uintptr_t)ws & 255) return fail(RPKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   }
-  int dev = 0;
-  int e = hipGetDevice(&dev);
-  if (e) return hip_fail(e, "hipGetDevice");
-  if (p->device >= 0 && p->device != dev)
-    return fail(RPKV_ERR_INVALID_ARG, "a plan is bound to the device of its first prepare");
-
-  // layout of the device copy
-  size_t off = 0;
-  p->off_pre = off;
-  off = align256(off + hp.prefill.size() * sizeof(Item));
-  p->off_dec = off;
-  off = align256(off + hp.decode.size() * sizeof(Item));
-  p->off_pbase = off;
-  off = align256(off + hp.tok_pbase.size() * sizeof(int32_t));
-  p->off_merge = off;
-  off = align256(off + hp.merge.size() * sizeof(int32_t));
-  p->off_tok = off;
-  off = align256(off + hp.toklist.size() * sizeof(int32_t));
-  p->off_indptr = off;
-  off = align256(off + hp.csr_indptr.size() * sizeof(int32_t));
-  const size_t bytes = std::max<size_t>(off, 256);
-
-  if (bytes > p->dmeta_cap) {
-    if (p->dmeta) {
-      e = hipStreamSynchronize((hipStream_t)stream);
-      if (e) return hip_fail(e, "hipStreamSynchronize");
-      e = hipFree(p->dmeta);
-      p->dmeta = nullptr;
-      p->dmeta_cap = 0;
-      if (e) return hip_fail(e, "hipFree");
-    }
-    const size_t cap = std::max(bytes, size_t(1) << 16);
-    e = hipMalloc((void **)&p->dmeta, cap);
-    if (e) return hip_fail(e, "hipMalloc (plan metadata)");
-    p->dmeta_cap = cap;
-  }
+  rpkv_status dst = ensure_device(p);
+  if (dst != RPKV_OK) return dst;
+  const rpkv::MetaLayout &lay = p->lay;
   const int c = p->hcur;
-  if (!p->hev[c]) {
-    e = hipEventCreateWithFlags(&p->hev[c], hipEventDisableTiming);
-    if (e) return hip_fail(e, "hipEventCreate");
-  }
-  if (p->hev_live[c]) {
+  int e = 0;
+  if (p->hev_live[c]) {  // the upload that last used this staging buffer
     e = hipEventSynchronize(p->hev[c]);
     if (e) return hip_fail(e, "hipEventSynchronize");
     p->hev_live[c] = false;
   }
-  if (bytes > p->hmeta_cap[c]) {
-    if (p->hmeta[c]) (void)hipHostFree(p->hmeta[c]);
-    p->hmeta[c] = nullptr;
-    p->hmeta_cap[c] = 0;
-    const size_t cap = std::max(bytes, size_t(1) << 16);
-    e = hipHostMalloc((void **)&p->hmeta[c], cap, hipHostMallocDefault);
-    if (e) return hip_fail(e, "hipHostMalloc (staging)");
-    p->hmeta_cap[c] = cap;
-  }
   char *h = p->hmeta[c];
+  const size_t bytes = lay.bytes;
   std::memset(h, 0, bytes);
-  if (!hp.prefill.empty()) std::memcpy(h + p->off_pre, hp.prefill.data(), hp.prefill.size() * sizeof(Item));
-  if (!hp.decode.empty()) std::memcpy(h + p->off_dec, hp.decode.data(), hp.decode.size() * sizeof(Item));
+  if (!hp.prefill.empty()) std::memcpy(h + lay.off_pre, hp.prefill.data(), hp.prefill.size() * sizeof(Item));
+  if (!hp.decode.empty()) std::memcpy(h + lay.off_dec, hp.decode.data(), hp.decode.size() * sizeof(Item));
   if (!hp.tok_pbase.empty())
-    std::memcpy(h + p->off_pbase, hp.tok_pbase.data(), hp.tok_pbase.size() * sizeof(int32_t));
-  if (!hp.merge.empty()) std::memcpy(h + p->off_merge, hp.merge.data(), hp.merge.size() * sizeof(int32_t));
+    std::memcpy(h + lay.off_pbase, hp.tok_pbase.data(), hp.tok_pbase.size() * sizeof(int32_t));
+  if (!hp.merge.empty()) std::memcpy(h + lay.off_merge, hp.merge.data(), hp.merge.size() * sizeof(int32_t));
   if (!hp.toklist.empty())
-    std::memcpy(h + p->off_tok, hp.toklist.data(), hp.toklist.size() * sizeof(int32_t));
+    std::memcpy(h + lay.off_tok, hp.toklist.data(), hp.toklist.size() * sizeof(int32_t));
   if (!hp.csr_indptr.empty())
-    std::memcpy(h + p->off_indptr, hp.csr_indptr.data(), hp.csr_indptr.size() * sizeof(int32_t));
+    std::memcpy(h + lay.off_indptr, hp.csr_indptr.data(), hp.csr_indptr.size() * sizeof(int32_t));
   e = hipMemcpyAsync(p->dmeta, h, bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
   if (e) return hip_fail(e, "hipMemcpyAsync (metadata)");
   e = hipEventRecord(p->hev[c], (hipStream_t)stream);
   if (e) return hip_fail(e, "hipEventRecord");
   p->hev_live[c] = true;
   p->hcur ^= 1;
-  p->meta_bytes = bytes;
-  p->device = dev;
   p->page_table = pt_dev;
   p->pt_stride = pt_stride;
   if (p->ws_need > 0) {
@@ -334,20 +344,14 @@ rpkv_status rpkv_prepare_metadata_csr(rpkv_plan *p, int32_t batch, const int32_t
       std::memcpy(host.data() + (size_t)i * cols, indices_host + indptr[i],
                   (size_t)(indptr[i + 1] - indptr[i]) * sizeof(int32_t));
   }
-  if (!p->csr_table) {
-    int e = hipMalloc((void **)&p->csr_table,
-                      std::max<size_t>(1, (size_t)p->s.max_batch * p->s.max_pages_per_req) * sizeof(int32_t));
-    if (e) {
-      p->csr_table = nullptr;
-      return hip_fail(e, "hipMalloc (dense copy of the CSR page table)");
-    }
-  }
+  rpkv_status dst = ensure_device(p);
+  if (dst != RPKV_OK) return dst;
   rpkv_status st = prepare_impl(p, batch, cu, L.data(), p->csr_table, p->s.max_pages_per_req, cols,
                                 indices_host ? host.data() : nullptr, groups, ngroups, ws, ws_bytes,
                                 stream, &iptr);
   if (st != RPKV_OK) return st;
   // expand the rows on the stream, after the upload of the offsets
-  const int e = rpkv::launch_csr_to_dense(batch, (const int32_t *)(p->dmeta + p->off_indptr),
+  const int e = rpkv::launch_csr_to_dense(batch, (const int32_t *)(p->dmeta + p->lay.off_indptr),
                                           indices_dev, p->csr_table, p->s.max_pages_per_req, stream);
   if (e) {
     p->prepared = false;
@@ -407,6 +411,9 @@ rpkv_status rpkv_plan_get_info(const rpkv_plan *p, rpkv_plan_info *info) {
   for (const rpkv::CascNode &nd : hp.tree) nm += (int64_t)nd.members.size();
   info->num_cascade_level_members = (int32_t)nm;
   info->tiles_per_block = hp.tiles_per_block;
+  info->metadata_bytes = (int64_t)p->lay.bytes;
+  info->metadata_capacity_bytes = (int64_t)p->meta_cap;
+  info->buffer_allocations = p->n_alloc;
   return RPKV_OK;
 }
 
@@ -469,9 +476,31 @@ rpkv_status rpkv_store_kv(rpkv_plan *p, const void *k, const void *v, const int3
     return fail(RPKV_ERR_INVALID_ARG, "k, v and pools must be 16-byte aligned");
   const int64_t row_bytes = (int64_t)p->s.Hkv * p->s.D * (p->s.dtype == RPKV_BF16 ? 2 : 4);
   const int64_t num_slots = p->s.num_pages * p->s.P;
+  if (p->s.check_slots) {
+    // debug mode: read the slots back once the stream has produced them
+    p->slots_host.resize((size_t)T);
+    int e = hipMemcpyAsync(p->slots_host.data(), slots, (size_t)T * sizeof(int32_t),
+                           hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (!e) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e) return hip_fail(e, "copying slot_mapping to the host (check_slots)");
+    std::string msg;
+    if (rpkv::find_bad_slot(p->slots_host.data(), T, num_slots, &p->slots_key, &msg) >= 0)
+      return fail(RPKV_ERR_INVALID_ARG, msg);
+  }
   return timed(p, RPKV_KERNEL_STORE, stream, [&] {
     return rpkv::launch_store_kv(k, v, slots, T, row_bytes, num_slots, kpool, vpool, stream);
   }, "store_kv launch");
+}
+
+rpkv_status rpkv_check_slot_mapping(const rpkv_plan *p, const int32_t *slots, int64_t T) {
+  if (!p) return fail(RPKV_ERR_INVALID_ARG, "plan is NULL");
+  if (T < 0 || (T > 0 && !slots)) return fail(RPKV_ERR_INVALID_ARG, "need num_tokens >= 0 and slots");
+  if (T > INT32_MAX) return fail(RPKV_ERR_INVALID_ARG, "num_tokens exceeds int32");
+  std::vector<int64_t> key;
+  std::string msg;
+  if (rpkv::find_bad_slot(slots, T, p->s.num_pages * p->s.P, &key, &msg) >= 0)
+    return fail(RPKV_ERR_INVALID_ARG, msg);
+  return RPKV_OK;
 }
 
 rpkv_status rpkv_attend(rpkv_plan *p, const void *q, const void *kpool, const void *vpool,
@@ -496,8 +525,8 @@ rpkv_status rpkv_attend(rpkv_plan *p, const void *q, const void *kpool, const vo
   a.out = out;
   a.page_table = p->page_table;
   a.pt_stride = p->pt_stride;
-  a.toklist = (const int32_t *)(p->dmeta + p->off_tok);
-  a.tok_pbase = (const int32_t *)(p->dmeta + p->off_pbase);
+  a.toklist = (const int32_t *)(p->dmeta + p->lay.off_tok);
+  a.tok_pbase = (const int32_t *)(p->dmeta + p->lay.off_pbase);
   a.o_part = p->o_part;
   a.lse_part = p->lse_part;
   a.Hq = p->s.Hq;
@@ -508,9 +537,9 @@ rpkv_status rpkv_attend(rpkv_plan *p, const void *q, const void *kpool, const vo
   a.num_pages = p->s.num_pages;
   a.scale_log2 = scale * 1.4426950408889634f;
   rpkv::AttnArgs pre = a, dec = a;
-  pre.items = (const Item *)(p->dmeta + p->off_pre);
+  pre.items = (const Item *)(p->dmeta + p->lay.off_pre);
   pre.n_items = (int32_t)hp.prefill.size();
-  dec.items = (const Item *)(p->dmeta + p->off_dec);
+  dec.items = (const Item *)(p->dmeta + p->lay.off_dec);
   dec.n_items = (int32_t)hp.decode.size();
   rpkv_status st = RPKV_OK;
   if (p->s.dtype == RPKV_BF16) {
@@ -532,7 +561,7 @@ rpkv_status rpkv_attend(rpkv_plan *p, const void *q, const void *kpool, const vo
                  "fp32 launch");
   }
   if (st == RPKV_OK && !hp.merge.empty()) {
-    const int32_t *mg = (const int32_t *)(p->dmeta + p->off_merge);
+    const int32_t *mg = (const int32_t *)(p->dmeta + p->lay.off_merge);
     st = timed(p, RPKV_KERNEL_MERGE, stream, [&] {
       return rpkv::launch_merge(mg, (int32_t)(hp.merge.size() / 3), p->o_part, p->lse_part, out,
                                 p->s.Hq, p->s.D, p->s.dtype, stream);
@@ -648,13 +677,14 @@ rpkv_status rpkv_graph_decode_forward(rpkv_plan *p, int32_t batch, const void *q
   a.num_pages = p->s.num_pages;
   a.scale_log2 = scale * 1.4426950408889634f;
   st = timed(p, RPKV_KERNEL_DECODE, stream, [&] {
-    return rpkv::launch_graph_decode_bf16(a, seq_lens, p->g_q_len, p->g_chunk, p->g_maxc, batch,
-                                          stream);
+    return rpkv::launch_graph_decode_bf16(a, seq_lens, p->g_q_len, p->g_chunk, p->g_maxc,
+                                          p->g_max_seq, batch, stream);
   }, "graph decode launch");
   if (st != RPKV_OK || p->g_maxc <= 1) return st;
   return timed(p, RPKV_KERNEL_MERGE, stream, [&] {
-    return rpkv::launch_graph_merge(seq_lens, p->g_q_len, p->g_chunk, p->g_maxc, T, p->g_opart,
-                                    p->g_lse, out, p->s.Hq, p->s.D, p->s.dtype, stream);
+    return rpkv::launch_graph_merge(seq_lens, p->g_q_len, p->g_chunk, p->g_maxc, p->g_max_seq, T,
+                                    p->g_opart, p->g_lse, out, p->s.Hq, p->s.D, p->s.dtype,
+                                    stream);
   }, "graph merge launch");
 }
 

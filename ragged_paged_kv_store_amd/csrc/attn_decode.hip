@@ -30,36 +30,41 @@ int launch_decode_bf16(const AttnArgs &a, void *stream) {
 // dispatched first and exit at once, the shorter last chunks of the long requests
 // follow, and the grid ends on full-length first chunks, so no stream of empty
 // wavefronts trails the work (measured: 2% faster than first-chunk-first).  L_i
-// comes from seq_lens on the device, so one captured launch serves any lengths up
-// to maxc * chunk.  Token t's partial c is row t * maxc + c.
+// comes from seq_lens on the device, so one captured launch serves any lengths in
+// [q_len, max_seq] (max_seq <= maxc * chunk); a request whose length is outside
+// that range is skipped (no key is read, its output rows are not written).
+// Token t's partial c is row t * maxc + c.
 template <class Slots>
 __global__ __launch_bounds__(256, 2) void attn_graph_decode_bf16_kernel(AttnArgs a,
                                                                         const int32_t *seq_lens,
                                                                         int32_t q_len, int32_t chunk,
-                                                                        int32_t maxc, int32_t batch) {
+                                                                        int32_t maxc, int32_t max_seq,
+                                                                        int32_t batch) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ii = blockIdx.x * kDecodeWavesPerBlock + wave;
   if (ii >= batch * maxc * a.Hkv) return;
   const int h = ii % a.Hkv, i = (ii / a.Hkv) % batch, c = maxc - 1 - ii / (a.Hkv * batch);
   const int L = seq_lens[i];
-  const int nch = min((L + chunk - 1) / chunk, maxc);
-  if (L < q_len || c >= nch) return;
+  if (L < q_len || L > max_seq) return;
+  const int nch = (L + chunk - 1) / chunk;  // <= maxc
+  if (c >= nch) return;
   const Item it{i, h, i * q_len, q_len, L - q_len, c * chunk, min(L, (c + 1) * chunk), nch > 1 ? c : -1};
   decode_item<Slots>(a, it);
 }
 
 int launch_graph_decode_bf16(const AttnArgs &a, const int32_t *seq_lens, int32_t q_len,
-                             int32_t chunk, int32_t maxc, int32_t batch, void *stream) {
+                             int32_t chunk, int32_t maxc, int32_t max_seq, int32_t batch,
+                             void *stream) {
   const int32_t n_items = batch * maxc * a.Hkv;
   if (n_items <= 0) return 0;
   const int blocks = (n_items + kDecodeWavesPerBlock - 1) / kDecodeWavesPerBlock;
   const dim3 grid(blocks), block(64 * kDecodeWavesPerBlock);
   if (a.log2P >= 4)
     hipLaunchKernelGGL(attn_graph_decode_bf16_kernel<dchunk::SlotsBig>, grid, block, 0,
-                       (hipStream_t)stream, a, seq_lens, q_len, chunk, maxc, batch);
+                       (hipStream_t)stream, a, seq_lens, q_len, chunk, maxc, max_seq, batch);
   else
     hipLaunchKernelGGL(attn_graph_decode_bf16_kernel<dchunk::SlotsSmall>, grid, block, 0,
-                       (hipStream_t)stream, a, seq_lens, q_len, chunk, maxc, batch);
+                       (hipStream_t)stream, a, seq_lens, q_len, chunk, maxc, max_seq, batch);
   return (int)hipGetLastError();
 }
 

@@ -163,34 +163,36 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t *__restrict__ 
                o_part, lse_part, out, Hq, dtype);
 }
 
-// The graph-decode merge: token t of a uniform batch has min(ceil(L_i / chunk),
-// maxc) partials at rows t * maxc + c (none to merge when there is one: the
-// chunk wrote the output).
+// The graph-decode merge: token t of a uniform batch has ceil(L_i / chunk) <=
+// maxc partials at rows t * maxc + c (none to merge when there is one: the chunk
+// wrote the output); requests with L_i outside [q_len, max_seq] were skipped.
 template <int D>
 __global__ __launch_bounds__(256) void graph_merge_kernel(const int32_t *__restrict__ seq_lens,
                                                           int32_t q_len, int32_t chunk, int32_t maxc,
+                                                          int32_t max_seq,
                                                           const float *__restrict__ o_part,
                                                           const float *__restrict__ lse_part,
                                                           void *__restrict__ out, int32_t Hq,
                                                           int32_t dtype) {
   const int32_t tok = blockIdx.x;
   const int32_t L = seq_lens[tok / q_len];
-  const int32_t ns = min((L + chunk - 1) / chunk, maxc);
-  if (ns <= 1 || L < q_len) return;
+  if (L < q_len || L > max_seq) return;
+  const int32_t ns = (L + chunk - 1) / chunk;  // <= maxc
+  if (ns <= 1) return;
   merge_one<D>(tok, tok * maxc, ns, o_part, lse_part, out, Hq, dtype);
 }
 
 int launch_graph_merge(const int32_t *seq_lens, int32_t q_len, int32_t chunk, int32_t maxc,
-                       int32_t T, const float *o_part, const float *lse_part, void *out,
+                       int32_t max_seq, int32_t T, const float *o_part, const float *lse_part, void *out,
                        int32_t Hq, int32_t D, int32_t dtype, void *stream) {
   if (T <= 0) return 0;
   const dim3 grid(T, (Hq + 3) / 4);
   if (D == 128)
     hipLaunchKernelGGL(graph_merge_kernel<128>, grid, dim3(256), 0, (hipStream_t)stream, seq_lens,
-                       q_len, chunk, maxc, o_part, lse_part, out, Hq, dtype);
+                       q_len, chunk, maxc, max_seq, o_part, lse_part, out, Hq, dtype);
   else
     hipLaunchKernelGGL(graph_merge_kernel<64>, grid, dim3(256), 0, (hipStream_t)stream, seq_lens,
-                       q_len, chunk, maxc, o_part, lse_part, out, Hq, dtype);
+                       q_len, chunk, maxc, max_seq, o_part, lse_part, out, Hq, dtype);
   return (int)hipGetLastError();
 }
 

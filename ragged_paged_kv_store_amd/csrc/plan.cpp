@@ -26,6 +26,7 @@
 //    (blocks are dealt round-robin to the 8 XCDs, each with its own L2), and
 //    each XCD's queue runs longest work first.
 #include <algorithm>
+#include <climits>
 #include <chrono>
 #include <cstring>
 #include <numeric>
@@ -61,6 +62,10 @@ rpkv_status check_shape(const rpkv_shape *s, Shape *o, std::string *msg) {
   }
   if (s->dtype == RPKV_BF16 && s->head_dim != 128) {
     *msg = "bf16 kernels are built for head_dim 128";
+    return RPKV_ERR_UNSUPPORTED;
+  }
+  if (s->dtype == RPKV_F32 && s->num_q_heads / s->num_kv_heads > kF32Rows) {
+    *msg = "fp32 kernels serve Hq / Hkv <= 16 (one 16-row tile per token)";
     return RPKV_ERR_UNSUPPORTED;
   }
   if (s->dtype == RPKV_F32 && s->head_dim != 64 && s->head_dim != 128) {
@@ -103,7 +108,112 @@ rpkv_status check_shape(const rpkv_shape *s, Shape *o, std::string *msg) {
   o->split_min_keys = (int32_t)round_up(s->split_min_keys ? s->split_min_keys : 64, kDecodeKeys);
   o->prefix_detect_keys = s->prefix_detect_keys;
   o->tiles_per_block = s->tiles_per_block;
+  o->check_slots = s->check_slots;
   return RPKV_OK;
+}
+
+// Slots are sorted together with their token index (packed in one 64-bit key),
+// so equal neighbours name a duplicate and its first two tokens.
+int64_t find_bad_slot(const int32_t *slots, int64_t n, int64_t num_slots,
+                      std::vector<int64_t> *scratch, std::string *msg) {
+  if (n > INT32_MAX) {
+    *msg = "slot_mapping longer than 2^31 - 1 tokens";
+    return 0;
+  }
+  std::vector<int64_t> &key = *scratch;
+  key.clear();
+  for (int64_t t = 0; t < n; ++t) {
+    const int32_t s = slots[t];
+    if (s < 0) continue;  // padding token
+    if (s >= num_slots) {
+      *msg = "slot_mapping[" + std::to_string(t) + "] = " + std::to_string(s) +
+             " is outside the pool of " + std::to_string(num_slots) + " slots";
+      return t;
+    }
+    key.push_back(((int64_t)s << 32) | t);
+  }
+  std::sort(key.begin(), key.end());
+  int64_t bad = -1, first = -1;
+  for (size_t k = 1; k < key.size(); ++k)
+    if ((key[k] >> 32) == (key[k - 1] >> 32)) {
+      const int64_t a = key[k - 1] & 0xFFFFFFFF, b = key[k] & 0xFFFFFFFF;
+      if (bad < 0 || b < bad) {
+        bad = b;
+        first = a;
+      }
+    }
+  if (bad >= 0)
+    *msg = "slot_mapping[" + std::to_string(bad) + "] repeats the slot of token " +
+           std::to_string(first) + " (" + std::to_string(slots[bad]) + ")";
+  return bad;
+}
+
+// Bounds on the work partition of any batch within the shape's capacities
+// (B requests, Tm tokens, rows of at most Lmax keys), following the rules below:
+//  * prefill-type tiles: sum over requests of ceil(n / tpt) per KV head, at most
+//    (ceil(Tm / tpt) + B) * Hkv; key splits add at most kPrefillSlots pieces
+//    (a tile of s steps becomes at most s / fair + 1 pieces, fair >= steps / 512);
+//  * cascade: a level holds decode-type tokens (n * G <= decode_max_rows), each
+//    in at most kMaxCascadeDepth levels, and there are fewer than B levels; the
+//    level tiles are at most kPrefillSlots + (tokens / tpt + levels) * Hkv (the
+//    level chunk is at least the levels' work / 512);
+//  * the XCD order pads to at most 2 * items + 16;
+//  * split-KV chunks: at most decode keys / chunk + one short chunk per
+//    (request, KV head), with chunk >= decode keys / split_target and >=
+//    split_min_keys;
+//  * per token one partial base and at most one merge record of 3 entries.
+MetaCounts meta_caps(const Shape &s) {
+  const int64_t G = s.G(), B = s.max_batch, Tm = s.max_tokens, Hkv = s.Hkv;
+  const int64_t tpt = std::max<int64_t>(1, (s.dtype == RPKV_F32 ? kF32Rows : kPrefillRows) / G);
+  const int64_t Lmax = (int64_t)s.max_pages_per_req * s.P;
+  const int64_t pieces = (cdiv(Tm, tpt) + B) * Hkv + kPrefillSlots;
+  const int64_t dtok = std::min<int64_t>(Tm, B * (s.decode_max_rows / G));
+  const int64_t tok = dtok * kMaxCascadeDepth;
+  const int64_t lev_tiles = tok > 0 ? kPrefillSlots + (cdiv(tok, tpt) + B) * Hkv : 0;
+  MetaCounts c{};
+  c.pre = 2 * (pieces + lev_tiles) + 2 * kNumXcd;
+  // B, Lmax and Hkv are each below 2^31: B * Lmax fits, the product with Hkv may not
+  const int64_t keys = B * Lmax;
+  const int64_t chunks = keys > INT64_MAX / Hkv ? INT64_MAX : cdiv(keys * Hkv, s.split_min_keys);
+  c.dec = dtok > 0 ? std::min<int64_t>(s.split_target, chunks) + B * Hkv : 0;
+  c.pbase = Tm;
+  c.merge = 3 * Tm;
+  c.tok = tok;
+  c.indptr = B + 1;
+  return c;
+}
+
+MetaCounts meta_counts(const HostPlan &p, int32_t max_batch) {
+  MetaCounts c{};
+  c.pre = (int64_t)p.prefill.size();
+  c.dec = (int64_t)p.decode.size();
+  c.pbase = (int64_t)p.tok_pbase.size();
+  c.merge = (int64_t)p.merge.size();
+  c.tok = (int64_t)p.toklist.size();
+  c.indptr = (int64_t)max_batch + 1;  // room for a CSR table's row offsets
+  return c;
+}
+
+// The device copy: items, split-KV items, token partial bases, merge records,
+// cascade token lists, CSR row offsets; each array 256-byte aligned.
+MetaLayout meta_layout(const MetaCounts &c) {
+  auto a256 = [](size_t x) { return (x + 255) & ~size_t(255); };
+  MetaLayout l{};
+  size_t off = 0;
+  l.off_pre = off;
+  off = a256(off + (size_t)c.pre * sizeof(Item));
+  l.off_dec = off;
+  off = a256(off + (size_t)c.dec * sizeof(Item));
+  l.off_pbase = off;
+  off = a256(off + (size_t)c.pbase * sizeof(int32_t));
+  l.off_merge = off;
+  off = a256(off + (size_t)c.merge * sizeof(int32_t));
+  l.off_tok = off;
+  off = a256(off + (size_t)c.tok * sizeof(int32_t));
+  l.off_indptr = off;
+  off = a256(off + (size_t)c.indptr * sizeof(int32_t));
+  l.bytes = std::max<size_t>(off, 256);
+  return l;
 }
 
 namespace {
@@ -176,6 +286,31 @@ void xcd_order(const std::vector<Item> &items, const std::vector<int64_t> &gkey,
     int best = (int)(std::min_element(load.begin(), load.end()) - load.begin());
     load[best] += p.work;
     q[best].insert(q[best].end(), p.members.begin(), p.members.end());
+  }
+  // Every queue is padded to the longest one's length; when the queues' item
+  // counts are very unequal (many short items against a few long ones) the
+  // shortest items of the fullest queues move to the emptiest, so the padded
+  // list holds at most 2 * n + 8 * per_block items (the plan's metadata buffer
+  // is sized for that bound).
+  {
+    const size_t cap = (size_t)round_up(cdiv((int64_t)(2 * n), kNumXcd), per_block);
+    size_t longest = 0;
+    for (auto &qq : q) longest = std::max(longest, qq.size());
+    if (longest > cap) {
+      for (int x = 0; x < kNumXcd; ++x) {
+        // the queue's items, shortest last
+        std::stable_sort(q[x].begin(), q[x].end(),
+                         [&](size_t a, size_t b) { return work[a] > work[b]; });
+      }
+      for (int x = 0; x < kNumXcd; ++x)
+        while (q[x].size() > cap) {
+          int y = 0;
+          for (int z = 1; z < kNumXcd; ++z)
+            if (q[z].size() < q[y].size()) y = z;
+          q[y].push_back(q[x].back());
+          q[x].pop_back();
+        }
+    }
   }
   // Within a queue: longest first by coarse work bucket (eighths of the queue's
   // longest item), and inside a bucket tiles sharing K/V together, so nearly
@@ -281,8 +416,10 @@ void detect_shared_prefixes(int32_t P, int32_t batch, int32_t cols, const int32_
 // Turns candidate levels into the level tree.  Candidates must nest (a range
 // inside another has a longer prefix; ranges may not overlap otherwise).  A
 // candidate becomes a level when at least two of its requests are eligible for
-// its prefix and it adds at least min_keys keys to the nearest level above it;
-// otherwise its nested candidates attach to that level.  Levels come out parents
+// its prefix, it adds at least min_keys keys to the nearest level above it, and
+// it lies at most kMaxCascadeDepth levels deep; otherwise its nested candidates
+// attach to that level (its keys then fall to the next level down or to the
+// members' own tails: the same result, read less often shared).  Levels come out parents
 // first, members ascending.
 template <class Eligible>
 rpkv_status nest_levels(std::vector<Span> spans, const std::vector<int32_t> &order,
@@ -297,6 +434,7 @@ rpkv_status nest_levels(std::vector<Span> spans, const std::vector<int32_t> &ord
     int32_t end, prefix, level;  // level: nearest level at or above, or -1
   };
   std::vector<Open> st;
+  std::vector<int32_t> depth;  // nesting depth of each level (1 at the top)
   tree->clear();
   for (const Span &sp : spans) {
     while (!st.empty() && st.back().end <= sp.lb) st.pop_back();
@@ -319,9 +457,11 @@ rpkv_status nest_levels(std::vector<Span> spans, const std::vector<int32_t> &ord
     for (int32_t k = sp.lb; k < end; ++k)
       if (eligible(order[k], sp.prefix)) members.push_back(order[k]);
     int32_t level = above;
-    if (members.size() >= 2 && sp.prefix - base >= min_keys) {
+    const int32_t d = above >= 0 ? depth[above] + 1 : 1;
+    if (members.size() >= 2 && sp.prefix - base >= min_keys && d <= kMaxCascadeDepth) {
       std::sort(members.begin(), members.end());
       tree->push_back(CascNode{above, sp.prefix, std::move(members)});
+      depth.push_back(d);
       level = (int32_t)tree->size() - 1;
     }
     st.push_back(Open{end, sp.prefix, level});

@@ -44,6 +44,9 @@ constexpr int kF32Rows = 16;          // fp32 tile rows
 constexpr int kF32Keys = 32;          // fp32 keys per LDS tile
 constexpr int kNumXcd = 8;            // MI355X: 8 XCDs, blocks go round-robin
 constexpr int kPrefillSlots = 512;    // MI355X: 256 CUs x 2 resident prefill tiles
+// deepest nesting of shared-prefix levels the planner keeps (the keys of deeper
+// levels are read by their members as part of the level above or their tails)
+constexpr int kMaxCascadeDepth = 16;
 // keys one split-KV wavefront streams while a co-resident MFMA tile runs one
 // 64-key step (measured rates: ~2.5 us per tile step, ~20 keys/us per chunk)
 constexpr int kConcurrentKeysPerStep = 24;
@@ -103,8 +106,27 @@ struct Shape {
   int64_t num_pages, max_tokens;
   int32_t decode_max_rows, split_target, split_min_keys, prefix_detect_keys;
   int32_t tiles_per_block;  // 0: chosen per batch
+  int32_t check_slots;      // debug: store_kv validates slot_mapping on the host
   int32_t G() const { return Hq / Hkv; }
 };
+
+// Entries of each array of the work partition's device copy.  meta_caps gives
+// the most any batch within a shape's capacities can need (the plan's device
+// buffers are sized from it once); meta_counts what one planned batch needs.
+struct MetaCounts {
+  int64_t pre, dec, pbase, merge, tok, indptr;
+};
+struct MetaLayout {
+  size_t off_pre, off_dec, off_pbase, off_merge, off_tok, off_indptr, bytes;
+};
+MetaCounts meta_caps(const Shape &s);
+MetaCounts meta_counts(const HostPlan &p, int32_t max_batch);
+MetaLayout meta_layout(const MetaCounts &c);
+
+// Validate a slot_mapping on the host: every non-negative slot below num_slots
+// and distinct.  Returns the first offending token or -1; `scratch` is reused.
+int64_t find_bad_slot(const int32_t *slots, int64_t n, int64_t num_slots,
+                      std::vector<int64_t> *scratch, std::string *msg);
 
 // Validate a shape; on failure returns the status and fills msg.
 rpkv_status check_shape(const rpkv_shape *s, Shape *out, std::string *msg);
@@ -145,9 +167,10 @@ int launch_decode_bf16(const AttnArgs &a, void *stream);
 int launch_fused_bf16(const AttnArgs &pre, const AttnArgs &dec, int tiles_per_block, void *stream);
 int launch_attn_f32(const AttnArgs &a, void *stream);
 int launch_graph_decode_bf16(const AttnArgs &a, const int32_t *seq_lens, int32_t q_len,
-                             int32_t chunk, int32_t maxc, int32_t batch, void *stream);
+                             int32_t chunk, int32_t maxc, int32_t max_seq, int32_t batch,
+                             void *stream);
 int launch_graph_merge(const int32_t *seq_lens, int32_t q_len, int32_t chunk, int32_t maxc,
-                       int32_t T, const float *o_part, const float *lse_part, void *out,
+                       int32_t max_seq, int32_t T, const float *o_part, const float *lse_part, void *out,
                        int32_t Hq, int32_t D, int32_t dtype, void *stream);
 int launch_csr_to_dense(int32_t B, const int32_t *indptr, const int32_t *indices, int32_t *dense,
                         int64_t stride, void *stream);

@@ -54,6 +54,10 @@ BASE = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, dtype=0,
     (dict(page_size=1), True),
     (dict(num_kv_heads=32), True),          # MHA
     (dict(num_kv_heads=1), True),           # G = 32
+    (dict(num_q_heads=128, num_kv_heads=1), True),   # G = 128, the largest
+    (dict(num_q_heads=256, num_kv_heads=1), False),
+    (dict(dtype=1, num_kv_heads=1), False),           # fp32 tiles hold 16 rows: G <= 16
+    (dict(dtype=1, num_q_heads=16, num_kv_heads=1), True),
     (dict(dtype=7), False),
     (dict(decode_max_rows=17), False),
 ])
