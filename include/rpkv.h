@@ -419,6 +419,32 @@ rpkv_status rpkv_graph_decode_forward(rpkv_plan *plan, int32_t batch, const void
                                       const int32_t *page_table, int64_t pt_stride,
                                       int32_t pt_cols, void *out, float scale, void *stream);
 
+/* rpkv_graph_decode_forward_noalloc: for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The step of rpkv_graph_decode_forward -- store_kv of the
+ * batch*q_len tokens, then split-KV attention merged by log-sum-exp -- with no
+ * rpkv_graph_decode_init and no allocation: q_len and max_seq_len are passed per
+ * call, the key chunk is the one rpkv_graph_decode_init(plan, batch, q_len,
+ * max_seq_len) would pick, and the split-KV partials live in a fixed 64 MiB
+ * device array inside the library (one per GPU, held until the process ends).
+ * Limits: bf16, q_len * Hq / Hkv <= 16, batch <= max_batch, batch * q_len <=
+ * max_tokens, max_seq_len <= max_pages_per_req * page_size, and the partials,
+ * batch * q_len * ceil(max_seq_len / chunk) * Hq * (D + 1) * 4 bytes (each part
+ * rounded up to 256), must fit 64 MiB, else RPKV_ERR_CAPACITY and nothing is
+ * enqueued.  Every call on a GPU reuses that GPU's array: calls that overlap on
+ * one GPU (other streams, other threads, other plans) race; calls ordered on
+ * one stream do not.  Nothing in the array needs clearing between calls (a
+ * call reads only partials it wrote).  Other arguments, their layouts and the
+ * length rule for seq_lens are those of rpkv_graph_decode_forward, with
+ * pt_cols >= ceil(max_seq_len / page_size). */
+rpkv_status rpkv_graph_decode_forward_noalloc(rpkv_plan *plan, int32_t batch, int32_t q_len,
+                                              int32_t max_seq_len, const void *q, const void *k,
+                                              const void *v, const int32_t *slot_mapping,
+                                              void *k_pool, void *v_pool,
+                                              const int32_t *seq_lens, const int32_t *page_table,
+                                              int64_t pt_stride, int32_t pt_cols, void *out,
+                                              float scale, void *stream);
+
 /* ------------------------------------------------- device-side metadata */
 
 /* Packed-batch metadata built on the device ("Variable-length batching and one

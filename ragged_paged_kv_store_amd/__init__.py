@@ -35,7 +35,7 @@ EXPORTS = (
     "rpkv_store_kv", "rpkv_attend", "rpkv_forward", "rpkv_timing_enable", "rpkv_timing_collect",
     "rpkv_build_metadata", "rpkv_graph_decode_init", "rpkv_graph_decode_forward",
     "rpkv_prepare_metadata_csr", "rpkv_rewrite_block_table", "rpkv_plan_get_cascade_tree",
-    "rpkv_check_slot_mapping",
+    "rpkv_check_slot_mapping", "rpkv_graph_decode_forward_noalloc",
 )
 
 
@@ -114,6 +114,8 @@ def _load():
         "rpkv_graph_decode_forward": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp,
                                             ctypes.c_float, vp]),
         "rpkv_check_slot_mapping": (i32, [vp, vp, i64]),
+        "rpkv_graph_decode_forward_noalloc": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                                    vp, i64, i32, vp, ctypes.c_float, vp]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(L, name)
@@ -490,6 +492,32 @@ class Plan:
             self._h, batch, _ptr(q), _ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(k_pool),
             _ptr(v_pool), seq_lens.data_ptr(), page_table.data_ptr(), page_table.stride(0),
             page_table.shape[1], _ptr(out), float(scale), _stream(stream)))
+
+    def graph_decode_forward_noalloc(self, batch: int, q_len: int, max_seq_len: int, q, k, v,
+                                     slot_mapping, k_pool, v_pool, seq_lens, page_table, out,
+                                     scale: float, stream=None):
+        """rpkv_graph_decode_forward_noalloc: the graph-decode step with no
+        graph_decode_init and no allocation (partials in the library's fixed
+        device array).  Shape checks only (no device reads)."""
+        import torch
+        T = batch * q_len
+        self._check_slots(slot_mapping, T)
+        self._check_rows("q", q, self.shape.num_q_heads, T)
+        self._check_rows("out", out, self.shape.num_q_heads, T)
+        self._check_rows("k", k, self.shape.num_kv_heads, T)
+        self._check_rows("v", v, self.shape.num_kv_heads, T)
+        self._check_pool("k_pool", k_pool)
+        self._check_pool("v_pool", v_pool)
+        if (not seq_lens.is_cuda or seq_lens.dtype != torch.int32 or seq_lens.numel() < batch
+                or not seq_lens.is_contiguous()):
+            raise ValueError("seq_lens: contiguous int32 device tensor with >= batch entries")
+        if (not page_table.is_cuda or page_table.dtype != torch.int32 or page_table.dim() != 2
+                or page_table.shape[0] < batch or page_table.stride(1) != 1):
+            raise ValueError("page_table: int32 device tensor [>= batch, cols], unit column stride")
+        _check(lib.rpkv_graph_decode_forward_noalloc(
+            self._h, batch, q_len, max_seq_len, _ptr(q), _ptr(k), _ptr(v), _ptr(slot_mapping),
+            _ptr(k_pool), _ptr(v_pool), seq_lens.data_ptr(), page_table.data_ptr(),
+            page_table.stride(0), page_table.shape[1], _ptr(out), float(scale), _stream(stream)))
 
     # ------------------------------------------------------- instrumentation
     def timing_enable(self, enable: bool, max_launches: int = 4096):

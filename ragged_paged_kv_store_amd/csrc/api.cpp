@@ -8,7 +8,7 @@
 #include <string>
 #include <vector>
 
-#include "rpkv_internal.h"
+#include "plan_state.h"
 
 using rpkv::HostPlan;
 using rpkv::Item;
@@ -17,6 +17,10 @@ using rpkv::Shape;
 namespace {
 thread_local std::string g_err;
 
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+}  // namespace
+
+namespace rpkv {
 rpkv_status fail(rpkv_status st, const std::string &msg) {
   g_err = msg;
   return st;
@@ -25,51 +29,12 @@ rpkv_status fail(rpkv_status st, const std::string &msg) {
 rpkv_status hip_fail(int err, const char *what) {
   return fail(RPKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString((hipError_t)err));
 }
+}  // namespace rpkv
 
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-}  // namespace
+using rpkv::fail;
+using rpkv::hip_fail;
+using rpkv::timed;
 
-struct rpkv_plan {
-  Shape s{};
-  HostPlan hp;
-  HostPlan hp_next;  // planned into, then swapped with hp when the batch is valid
-  bool planned = false;
-  bool prepared = false;
-  int device = -1;
-  // device copy of the work partition, sized once for the shape's capacities
-  // (rpkv::meta_caps) at the first prepare; every batch's copy fits in it
-  char *dmeta = nullptr;
-  size_t meta_cap = 0;        // bytes of dmeta and of each staging buffer
-  rpkv::MetaLayout lay{};     // the planned batch's layout
-  int64_t n_alloc = 0;        // allocations made by ensure_device
-  // dense copy of a CSR page table (plan-owned, [max_batch, max_pages_per_req])
-  int32_t *csr_table = nullptr;
-  // pinned staging, two buffers so a new batch never overwrites one in flight
-  char *hmeta[2] = {nullptr, nullptr};
-  hipEvent_t hev[2] = {nullptr, nullptr};
-  bool hev_live[2] = {false, false};
-  int hcur = 0;
-  // bound per batch
-  const int32_t *page_table = nullptr;
-  int64_t pt_stride = 0;
-  float *o_part = nullptr;
-  float *lse_part = nullptr;
-  size_t ws_need = 0;
-  // timing
-  bool timing = false;
-  int32_t max_launches = 0;
-  std::vector<hipEvent_t> ev;
-  std::vector<int32_t> ev_kind;
-  int32_t n_rec = 0;
-  // host copy of a slot_mapping for the check_slots debug mode
-  std::vector<int32_t> slots_host;
-  std::vector<int64_t> slots_key;
-  // graph-capturable decode: fixed capacities and plan-owned partials
-  int32_t g_max_batch = 0, g_q_len = 0, g_chunk = 0, g_maxc = 0, g_max_seq = 0;
-  float *g_opart = nullptr;
-  float *g_lse = nullptr;
-  int g_device = -1;
-};
 
 namespace {
 
@@ -95,22 +60,6 @@ void release_device(rpkv_plan *p) {
   p->device = -1;
 }
 
-template <class F>
-rpkv_status timed(rpkv_plan *p, int kind, void *stream, F &&launch, const char *what) {
-  const bool rec = p->timing && p->n_rec < p->max_launches;
-  if (rec) {
-    int e = hipEventRecord(p->ev[2 * p->n_rec], (hipStream_t)stream);
-    if (e) return hip_fail(e, "hipEventRecord");
-  }
-  int err = launch();
-  if (err) return hip_fail(err, what);
-  if (rec) {
-    int e = hipEventRecord(p->ev[2 * p->n_rec + 1], (hipStream_t)stream);
-    if (e) return hip_fail(e, "hipEventRecord");
-    p->ev_kind[p->n_rec++] = kind;
-  }
-  return RPKV_OK;
-}
 
 }  // namespace
 
@@ -594,13 +543,8 @@ rpkv_status rpkv_graph_decode_init(rpkv_plan *p, int32_t max_batch, int32_t q_le
     return fail(RPKV_ERR_CAPACITY, "max_seq_len exceeds max_pages_per_req * page_size");
   if ((int64_t)max_batch * q_len > INT32_MAX / 32)
     return fail(RPKV_ERR_INVALID_ARG, "max_batch * q_len too large");
-  // Chunks per request: enough that a full batch gives about 4 wavefronts per
-  // resident slot (2048 on the chip), between 2 and 32 (the merge's
-  // one-round-trip path); chunks of >= 256 keys, a multiple of 64.
-  const int64_t waves_per_chunk = (int64_t)max_batch * p->s.Hkv;
-  const int32_t want = (int32_t)std::min<int64_t>(32, std::max<int64_t>(2, (8192 + waves_per_chunk - 1) / waves_per_chunk));
-  const int32_t chunk = std::max<int32_t>(256, (int32_t)(((max_seq_len + want - 1) / want + 63) / 64 * 64));
-  const int32_t maxc = (max_seq_len + chunk - 1) / chunk;
+  int32_t chunk = 0, maxc = 0;
+  rpkv::graph_decode_chunks(max_batch, p->s.Hkv, max_seq_len, &chunk, &maxc);
   int dev = 0;
   int e = hipGetDevice(&dev);
   if (e) return hip_fail(e, "hipGetDevice");

@@ -112,6 +112,14 @@ rpkv_status check_shape(const rpkv_shape *s, Shape *o, std::string *msg) {
   return RPKV_OK;
 }
 
+void graph_decode_chunks(int64_t max_batch, int32_t Hkv, int32_t max_seq, int32_t *chunk,
+                         int32_t *maxc) {
+  const int64_t waves_per_chunk = std::max<int64_t>(1, max_batch * Hkv);
+  const int64_t want = std::min<int64_t>(32, std::max<int64_t>(2, cdiv(8192, waves_per_chunk)));
+  *chunk = (int32_t)std::max<int64_t>(256, round_up(cdiv(max_seq, want), 64));
+  *maxc = (int32_t)cdiv(max_seq, *chunk);
+}
+
 // Slots are sorted together with their token index (packed in one 64-bit key),
 // so equal neighbours name a duplicate and its first two tokens.
 int64_t find_bad_slot(const int32_t *slots, int64_t n, int64_t num_slots,

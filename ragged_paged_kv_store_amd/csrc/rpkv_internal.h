@@ -128,6 +128,14 @@ MetaLayout meta_layout(const MetaCounts &c);
 int64_t find_bad_slot(const int32_t *slots, int64_t n, int64_t num_slots,
                       std::vector<int64_t> *scratch, std::string *msg);
 
+// Key chunk of the graph-capturable decode for batches of up to max_batch
+// requests with lengths up to max_seq: chunks per request enough that a full
+// batch gives about 4 wavefronts per resident slot (2048 on the chip), between 2
+// and 32 (the merge's one-round-trip path); chunks of >= 256 keys, a multiple
+// of 64.  *maxc = ceil(max_seq / chunk).
+void graph_decode_chunks(int64_t max_batch, int32_t Hkv, int32_t max_seq, int32_t *chunk,
+                         int32_t *maxc);
+
 // Validate a shape; on failure returns the status and fills msg.
 rpkv_status check_shape(const rpkv_shape *s, Shape *out, std::string *msg);
 
