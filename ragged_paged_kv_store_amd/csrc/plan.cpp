@@ -31,6 +31,7 @@
 #include <cstring>
 #include <numeric>
 #include <string>
+#include <tuple>
 
 #include "rpkv_internal.h"
 
@@ -159,13 +160,16 @@ int64_t find_bad_slot(const int32_t *slots, int64_t n, int64_t num_slots,
 // Bounds on the work partition of any batch within the shape's capacities
 // (B requests, Tm tokens, rows of at most Lmax keys), following the rules below:
 //  * prefill-type tiles: sum over requests of ceil(n / tpt) per KV head, at most
-//    (ceil(Tm / tpt) + B) * Hkv; key splits add at most kPrefillSlots pieces
-//    (a tile of s steps becomes at most s / fair + 1 pieces, fair >= steps / 512);
+//    (ceil(Tm / tpt) + B) * Hkv; key splits make at most twice that plus
+//    kPrefillSlots pieces (a tile becomes at most s / fair + 1 pieces, s the
+//    steps of the longer of it and its sibling, at most 3 more than its own,
+//    fair >= 8 and >= total steps / 512);
 //  * cascade: a level holds decode-type tokens (n * G <= decode_max_rows), each
 //    in at most kMaxCascadeDepth levels, and there are fewer than B levels; the
 //    level tiles are at most kPrefillSlots + (tokens / tpt + levels) * Hkv (the
 //    level chunk is at least the levels' work / 512);
-//  * the XCD order pads to at most 2 * items + 16;
+//  * the XCD order pads to at most 2 * items + 16 single items, or 2 * units + 8
+//    workgroups of two siblings (units <= items), i.e. 4 * items + 16;
 //  * split-KV chunks: at most decode keys / chunk + one short chunk per
 //    (request, KV head), with chunk >= decode keys / split_target and >=
 //    split_min_keys;
@@ -174,12 +178,12 @@ MetaCounts meta_caps(const Shape &s) {
   const int64_t G = s.G(), B = s.max_batch, Tm = s.max_tokens, Hkv = s.Hkv;
   const int64_t tpt = std::max<int64_t>(1, (s.dtype == RPKV_F32 ? kF32Rows : kPrefillRows) / G);
   const int64_t Lmax = (int64_t)s.max_pages_per_req * s.P;
-  const int64_t pieces = (cdiv(Tm, tpt) + B) * Hkv + kPrefillSlots;
+  const int64_t pieces = 2 * (cdiv(Tm, tpt) + B) * Hkv + kPrefillSlots;
   const int64_t dtok = std::min<int64_t>(Tm, B * (s.decode_max_rows / G));
   const int64_t tok = dtok * kMaxCascadeDepth;
   const int64_t lev_tiles = tok > 0 ? kPrefillSlots + (cdiv(tok, tpt) + B) * Hkv : 0;
   MetaCounts c{};
-  c.pre = 2 * (pieces + lev_tiles) + 2 * kNumXcd;
+  c.pre = 4 * (pieces + lev_tiles) + 2 * kNumXcd;
   // B, Lmax and Hkv are each below 2^31: B * Lmax fits, the product with Hkv may not
   const int64_t keys = B * Lmax;
   const int64_t chunks = keys > INT64_MAX / Hkv ? INT64_MAX : cdiv(keys * Hkv, s.split_min_keys);
@@ -235,14 +239,13 @@ int64_t item_work(const Item &it) {
 // stay on one XCD, groups larger than a fair share are cut into contiguous
 // pieces, pieces are placed longest-first on the least loaded queue, each queue
 // runs longest-first, and the queues are interleaved so block b runs on XCD b%8.
-void xcd_order(const std::vector<Item> &items, const std::vector<int64_t> &gkey, int per_block,
-               std::vector<Item> *outp) {
-  std::vector<Item> &out = *outp;
+// The result is the launch order as indices into the items, -1 for padding.
+void xcd_order(const std::vector<int64_t> &work, const std::vector<int64_t> &gkey, int per_block,
+               std::vector<int32_t> *outp) {
+  std::vector<int32_t> &out = *outp;
   out.clear();
-  if (items.empty()) return;
-  const size_t n = items.size();
-  std::vector<int64_t> work(n);
-  for (size_t k = 0; k < n; ++k) work[k] = item_work(items[k]);
+  if (work.empty()) return;
+  const size_t n = work.size();
   // items sharing K/V together, in ascending key order (the planner emits them
   // that way, so this is usually the identity); ties keep the input order
   std::vector<size_t> idx(n);
@@ -347,14 +350,12 @@ void xcd_order(const std::vector<Item> &items, const std::vector<int64_t> &gkey,
   }
   // workgroup b runs on XCD b % 8 and takes per_block consecutive items:
   // items k..k+per_block-1 of queue x go to workgroup (k / per_block) * 8 + x
-  Item pad{};
-  pad.ntok = 0;
   const size_t per = (size_t)per_block;
   qlen = (qlen + per - 1) / per * per;
-  out.assign(qlen * kNumXcd, pad);
+  out.assign(qlen * kNumXcd, -1);
   for (int x = 0; x < kNumXcd; ++x)
     for (size_t k = 0; k < q[x].size(); ++k)
-      out[((k / per) * kNumXcd + x) * per + k % per] = items[q[x][k]];
+      out[((k / per) * kNumXcd + x) * per + k % per] = (int32_t)q[x][k];
 }
 
 // A candidate level: positions [lb, lb + cnt) of a request order share `prefix`
@@ -660,28 +661,37 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
   // A tile much longer than the fair share of steps per concurrent tile slot
   // would set the launch's critical path: cut its key range into pieces of whole
   // 64-key steps, merged afterwards like split-KV chunks.  (Not for fp32.)
+  // Sibling tiles (consecutive row blocks of one request and KV head) are cut
+  // at the same keys, from the longer one's length, so a workgroup running two
+  // of them can share one K/V stream.
   const int64_t fair = std::max<int64_t>(8, cdiv(total_steps, kPrefillSlots));
-  for (size_t k = 0; k < tiles.size(); ++k) {
-    const Item &t = tiles[k];
-    const int64_t steps = cdiv(t.kend, kPrefillKeys);
+  for (size_t k = 0; k < tiles.size();) {
+    const bool sib = k + 1 < tiles.size() && tile_key[k + 1] == tile_key[k];
+    const size_t kn = sib ? k + 2 : k + 1;
+    int64_t steps = 0;
+    for (size_t u = k; u < kn; ++u) steps = std::max<int64_t>(steps, cdiv(tiles[u].kend, kPrefillKeys));
     int64_t parts = f32 ? 1 : cdiv(steps, fair);
     if (steps <= fair + fair / 2) parts = 1;
-    if (parts <= 1) {
-      pre.push_back(t);
-      pre_key.push_back(tile_key[k]);
-      continue;
+    const int64_t per = cdiv(steps, std::max<int64_t>(parts, 1)) * kPrefillKeys;
+    for (size_t u = k; u < kn; ++u) {
+      const Item &t = tiles[u];
+      const int64_t tparts = parts <= 1 ? 1 : cdiv(t.kend, per);
+      if (tparts <= 1) {
+        pre.push_back(t);
+        pre_key.push_back(tile_key[u]);
+        continue;
+      }
+      for (int32_t tk = t.tok0; tk < t.tok0 + t.ntok; ++tk) nsplit[tk] = (int32_t)tparts;
+      for (int64_t pc = 0; pc < tparts; ++pc) {
+        Item piece = t;
+        piece.kbeg = (int32_t)(pc * per);
+        piece.kend = (int32_t)std::min<int64_t>(t.kend, (pc + 1) * per);
+        piece.split = (int32_t)pc;
+        pre.push_back(piece);
+        pre_key.push_back(tile_key[u]);
+      }
     }
-    const int64_t per = cdiv(steps, parts) * kPrefillKeys;
-    parts = cdiv(t.kend, per);
-    for (int32_t tk = t.tok0; tk < t.tok0 + t.ntok; ++tk) nsplit[tk] = (int32_t)parts;
-    for (int64_t pc = 0; pc < parts; ++pc) {
-      Item piece = t;
-      piece.kbeg = (int32_t)(pc * per);
-      piece.kend = (int32_t)std::min<int64_t>(t.kend, (pc + 1) * per);
-      piece.split = (int32_t)pc;
-      pre.push_back(piece);
-      pre_key.push_back(tile_key[k]);
-    }
+    k = kn;
   }
 
   // level tiles: each level's members stacked against the keys it adds.  One
@@ -837,7 +847,59 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
       tpb = !pre.empty() && steps >= (int64_t)kPairMinSteps * (int64_t)pre.size() ? 2 : 1;
     }
     p.tiles_per_block = tpb;
-    xcd_order(pre, pre_key, tpb, &p.prefill);
+    Item pad{};
+    std::vector<int64_t> &work = p.tmp.work;
+    std::vector<int32_t> &order = p.tmp.order;
+    if (tpb == 1) {
+      work.resize(pre.size());
+      for (size_t k = 0; k < pre.size(); ++k) work[k] = item_work(pre[k]);
+      xcd_order(work, pre_key, 1, &order);
+      p.prefill.resize(order.size());
+      for (size_t b = 0; b < order.size(); ++b) p.prefill[b] = order[b] >= 0 ? pre[order[b]] : pad;
+    } else {
+      // Workgroups of two sibling items sharing one K/V stream: the same
+      // request (or cascade level) and KV head, the same first key, and for
+      // cascade level tiles the same last key; consecutive row blocks pair up,
+      // an unpaired item runs with an empty partner.  The units are ordered like
+      // single items, by the longer of the two ranges.
+      std::vector<int32_t> &idx = p.tmp.idx;
+      idx.resize(pre.size());
+      std::iota(idx.begin(), idx.end(), 0);
+      auto unit_of = [&](int32_t k) {
+        const Item &it = pre[k];
+        const bool casc = it.pos0 < 0;
+        return std::make_tuple(pre_key[k], casc, it.kbeg, casc ? it.kend : 0);
+      };
+      std::sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) {
+        const auto ux = unit_of(x), uy = unit_of(y);
+        return ux != uy ? ux < uy : pre[x].tok0 < pre[y].tok0;
+      });
+      std::vector<int32_t> &second = p.tmp.second;
+      std::vector<int64_t> &ukey = p.tmp.ukey;
+      std::vector<int32_t> &first = p.tmp.first;
+      first.clear();
+      second.clear();
+      ukey.clear();
+      work.clear();
+      for (size_t k = 0; k < idx.size();) {
+        const int32_t x = idx[k];
+        const bool pair = k + 1 < idx.size() && unit_of(idx[k + 1]) == unit_of(x);
+        const int32_t y = pair ? idx[k + 1] : -1;
+        first.push_back(x);
+        second.push_back(y);
+        ukey.push_back(pre_key[x]);
+        const int32_t kend = pair ? std::max(pre[x].kend, pre[y].kend) : pre[x].kend;
+        work.push_back(cdiv(std::max(kend - pre[x].kbeg, 1), kPrefillKeys));
+        k += pair ? 2 : 1;
+      }
+      xcd_order(work, ukey, 1, &order);
+      p.prefill.resize(2 * order.size());
+      for (size_t b = 0; b < order.size(); ++b) {
+        const int32_t u = order[b];
+        p.prefill[2 * b] = u >= 0 ? pre[first[u]] : pad;
+        p.prefill[2 * b + 1] = u >= 0 && second[u] >= 0 ? pre[second[u]] : pad;
+      }
+    }
   }
   std::swap(p.decode, dec);
   p.plan_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_start)

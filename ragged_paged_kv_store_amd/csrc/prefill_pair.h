@@ -1,26 +1,32 @@
-// bf16 MFMA attention tiles, two per workgroup in ping-pong.
+// bf16 MFMA attention tiles, two per workgroup in ping-pong, sharing K/V.
 //
-// A workgroup of 8 wavefronts runs two independent tiles (items 2p and 2p+1 of
-// the prefill list), one per group of 4 wavefronts; wavefronts w and w+4 share
-// a SIMD.  Each tile's work per 64-key step splits into a matrix phase (the
+// A workgroup of 8 wavefronts runs two tiles (items 2p and 2p+1 of the prefill
+// list), one per group of 4 wavefronts; wavefronts w and w+4 share a SIMD.  The
+// two tiles are siblings: query rows of the same request and KV head over the
+// same first key (adjacent row blocks of one causal chunk, or of one cascade
+// level chunk), so one stream of K/V rows staged in LDS serves both; the planner
+// pairs them (an unpaired tile gets an empty partner, whose group then only
+// loads).  Each tile's work per 64-key step splits into a matrix phase (the
 // MFMAs of S(t) = K(t) Q^T and of O += P(t-1) V(t-1)) and a vector phase (the
-// online softmax of S(t) and the issue of later K/V loads).  The two groups run
+// online softmax of S(t) and the issue of later loads).  The two groups run
 // these phases in opposite order, separated by workgroup barriers, so on every
 // SIMD one wavefront issues MFMAs while its partner does the softmax.
 //
 // Tile layout, masking, softmax and operand formats are those of the 4-wavefront
-// tile (prefill_tile.h); only the schedule differs:
-//   round r, group 0:  G(r) | V(r)          group 1:  V(r-1) | G(r)
-//   G(r): S(r) from K buffer r%2, then O += P(r-1) V(r-1) from V buffer
-//         (r-1)%2 (S(r) is complete by the time the vector phase reads it)
-//   V(r): loads of K(r+2) into K buffer r%2 and of V(r+1) into V buffer
-//         (r+1)%2; softmax of S(r) into P(r); wait for the loads issued in
-//         V(r-1), which G(r+1) reads; page ids of step r+3.
-// A tile of T steps runs rounds 0..T (G(T) is the last PV product) and writes
-// its output right after round T.
-// A buffer is refilled only after the barrier that ends the phase reading it,
-// and loads have two phases to land.  A group whose tile has fewer steps keeps
-// taking part in the barriers.
+// tile (prefill_tile.h); only the schedule differs.  With half-round h:
+//   round r, group 0:  G(r) [h = 2r]   | V(r)   [h = 2r+1]
+//            group 1:  V(r-1) [h = 2r] | G(r)   [h = 2r+1]
+//   G(r): S(r) from K(r), then O += P(r-1) V(r-1)
+//   V(r): softmax of S(r) into P(r); group 0 loads K(r+2), group 1 loads
+//         V(r+2) (four 1 KiB loads per wavefront); then the wait for the loads
+//         this group issued in its previous vector phase.
+// Step t's K and V sit in buffer t%3 of three: K(t) is read in half-rounds
+// 2t and 2t+1 and refilled (with K(t+3)) in 2t+3; V(t) is read in 2t+2 and
+// 2t+3 and refilled in 2t+4; every load has two half-rounds to land, and the
+// barrier after the wait that covers it publishes it to the other group.  Both
+// groups run the steps of the union of their key ranges; a group whose own range
+// ends earlier masks the keys past it.  A tile of T steps runs rounds 0..T (G(T)
+// is the last PV product) and writes its output right after round T.
 #pragma once
 
 #include <type_traits>
@@ -35,19 +41,12 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 }  // namespace ppair
 
 template <int PM, int GRP>
-__device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, const int T,
-                                           const int R, const int lw) {
+__device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, const int kbeg,
+                                           const int kend_u, const int T, unsigned char *Kbuf,
+                                           unsigned char *Vbuf, const int lw) {
   using namespace ptile;
   constexpr bool BIGPAGE = PM == 2;
-  constexpr int NIDS = BIGPAGE ? 0 : 4;  // vector loads per page-id fetch
-  // per-group buffers (each instantiation has its own), addressed statically
-  __shared__ __attribute__((aligned(1024))) unsigned char K0[BUFB], K1[BUFB];
-  __shared__ __attribute__((aligned(1024))) unsigned char V0[BUFB], V1[BUFB];
-
-  if (T == 0) {  // no tile: keep the barrier count of the partner group
-    for (int i = 0; i < 2 * R + 3; ++i) __builtin_amdgcn_s_barrier();
-    return;
-  }
+  const bool own = it.ntok > 0;  // false: this group only loads (no tile)
   const int lane = threadIdx.x & 63;
   const int q32 = lane & 31, half = lane >> 5;
   const int G = a.G;
@@ -56,13 +55,14 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
 
   const int m = lw * 32 + q32;
   const bool rowv = m < rows;
-  const int tl = rowv ? m / G : it.ntok - 1;
+  // (a group without a tile reads no token data)
+  const int tl = rowv ? m / G : (own ? it.ntok - 1 : 0);
   const int gg = rowv ? m % G : 0;
-  const int tok = casc ? a.toklist[it.tok0 + tl] : it.tok0 + tl;
+  const int tok = !own ? 0 : casc ? a.toklist[it.tok0 + tl] : it.tok0 + tl;
   const int qh = it.kvh * G + gg;
   const int apos = casc ? INT32_MAX : it.pos0 + tl;
   const int amin = casc ? INT32_MAX : it.pos0;
-  const int32_t pbase = it.split >= 0 ? a.tok_pbase[tok] : 0;
+  const int32_t pbase = own && it.split >= 0 ? a.tok_pbase[tok] : 0;
 
   bf16x8 qf[8];  // this lane's Q row, loaded in the prologue
 
@@ -81,7 +81,9 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
   const char *vpool = (const char *)a.vpool;
   const int64_t row_bytes = (int64_t)a.Hkv * (D * 2);
   const int64_t head_off = (int64_t)it.kvh * (D * 2);
-  const int kbeg = it.kbeg, kend = it.kend;
+  // loads address the union of the two tiles' key ranges; the group's own end
+  // masks its logits
+  const int kend = kend_u, kend_own = it.kend;
 
   // page ids of one step's loads (see prefill_tile.h): one per wavefront for
   // big pages, a scalar load (the page table is constant during the launch;
@@ -196,34 +198,42 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
 
   f32x16 s[2];
   bf16x8 pf[2][2];
-  // page ids by step parity: at the start of V(r), ids[r%2] holds step r+2's
-  // (K load) and ids[(r+1)%2] step r+1's (V load), which is then refetched for
-  // step r+3; no id is ever copied, so no copy waits on its load
-  Ids ids[2];
+  // this group's share of the loads: K rows (group 0) or V rows (group 1) of
+  // each step, rows 16*lw.. of the buffer of the step
+  const char *pool = GRP == 0 ? kpool : vpool;
+  unsigned char *const LB = GRP == 0 ? Kbuf : Vbuf;
+  // page ids of the step the next vector phase loads (fetched at the end of the
+  // vector phase before it; one slot, never copied)
+  Ids ids;
 
-  // ---- prologue: K(0), V(0), K(1) loaded, ids of step 2 requested
+  // ---- prologue: steps 0 and 1 of this group's share loaded, ids of step 2
+  // requested
   {
-    Ids i0;
+    Ids i0, i1;
     fetch_ids(i0, kbeg);
-    fetch_ids(ids[1], kbeg + BN);  // clamped in range when the tile has one step
-    issue(i0, 0, kpool, K0);
-    issue(i0, 0, vpool, V0);
-    if (T > 1) issue(ids[1], 1, kpool, K1);
-    ids[0] = i0;  // (a valid page for the loads past a short tile's end)
-    if (T > 2) fetch_ids(ids[0], kbeg + 2 * BN);
-    // the Q row goes out beside the first K/V loads, and one wait covers them
+    fetch_ids(i1, kbeg + BN);  // clamped in range when there is one step
+    issue(i0, 0, pool, LB);
+    issue(i1, 1, pool, LB + BUFB);
+    fetch_ids(ids, kbeg + 2 * BN);
+    // the Q row goes out beside the first loads, and one wait covers them
     // all: past it the compiler sees no vector load of its own pending (it
     // cannot see the K/V loads, and would otherwise wait on them for Q)
-    const uint16_t *qrow = (const uint16_t *)a.q + ((int64_t)tok * a.Hq + qh) * D;
+    if (own) {
+      const uint16_t *qrow = (const uint16_t *)a.q + ((int64_t)tok * a.Hq + qh) * D;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*(const u32x4 *)(qrow + 16 * s + 8 * half));
+      for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*(const u32x4 *)(qrow + 16 * s + 8 * half));
+    }
     __builtin_amdgcn_s_waitcnt(ppair::vmcnt_imm(0));
   }
   __builtin_amdgcn_s_barrier();
 
   // ---- matrix phase of round r
-  auto gphase = [&](int r, const unsigned char *Kb, const unsigned char *Vp) {
-    if (r > T) return;
+  // (B: r % 3, a compile-time constant in the unrolled loop below, so every
+  // LDS address is a fixed offset)
+  auto gphase = [&](int r, auto B) {
+    if (!own || r > T) return;
+    const unsigned char *Kb = Kbuf + B.value * BUFB;
+    const unsigned char *Vp = Vbuf + ((B.value + 2) % 3) * BUFB;  // V(r-1)
     if (r < T) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -244,12 +254,16 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kf[st % 3][kb], qf[st], s[kb]);
       }
+      // each K read right after the MFMA that consumed the register it refills
+      // (0x100: LDS reads, 0x8: MFMA)
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        if (st + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
+      for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (st + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       // the products stay in this phase
       asm volatile("" : "+v"(s[0]), "+v"(s[1]));
     }
@@ -267,12 +281,18 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
                 bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             o[db] = mfma32(vf, pf[kb][s2], o[db]);
           }
+      // the two transposing reads of the next block's V^T fragment db right after
+      // the MFMA that consumed this block's fragment db: each read has the
+      // remaining three MFMAs of the block to land, and the wavefront never
+      // issues a run of MFMAs with no reads of the next block in flight
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
-        if (blk + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
-      }
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          if (blk + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
     }
   };
 
@@ -311,8 +331,8 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
   // after each of the first three 16-key blocks of exponentials (h = 1..3)
   auto softmax = [&](int r, auto &&hook) {
     const int kt = kbeg + r * BN;
-    if ((kt + BN - 1 > amin) || (kt + BN > kend)) {
-      const int rel = min(kend - 1, apos) - kt - 4 * half;
+    if ((kt + BN - 1 > amin) || (kt + BN > kend_own)) {
+      const int rel = min(kend_own - 1, apos) - kt - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -363,107 +383,88 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
     lrun += sum0 + sum1;
   };
 
-  // ---- vector phase of round r: Kn = K buffer r%2, Vn = V buffer (r+1)%2;
-  // P = r%2 (the parity is static in the unrolled loop).  With big pages the 8
-  // loads go out two at a time between parts of the softmax, so their issue
-  // (the address unit takes a while per 1 KiB load, and four wavefronts issue
-  // together) overlaps the exponentials; with small pages they go out first.
-  auto vphase = [&](int r, auto P, unsigned char *Kn, unsigned char *Vn) {
+  // ---- vector phase of round r: the group's four loads of step r+2 into
+  // buffer (r+2)%3 (read last in half-round 2r-1 for K, 2r+1 for V), the
+  // softmax of S(r), the wait for the loads of the previous vector phase, the
+  // ids of step r+3.  With big pages the loads go out one between each part of
+  // the softmax, from a scalar base plus 32-bit lane offsets (past the range
+  // end they refill a buffer nobody reads); with small pages they go out first.
+  auto vphase = [&](int r, auto B) {
     if (r < 0 || r >= T) return;
-    const bool f_ids = r + 3 < T, f_k = r + 2 < T, f_v = r + 1 < T;
+    unsigned char *dst = LB + ((B.value + 2) % 3) * BUFB;
     if (BIGPAGE) {
-      // big pages: all 8 loads always go out (past the tile's last step they
-      // refill buffers nobody reads), two at a time between parts of the
-      // softmax, each from a scalar base plus a 32-bit lane offset
-      uint32_t ok[4], ov[4];
-      const char *sbk = step_addr(ids[P.value], r + 2, kpool, ok);
-      const char *sbv = step_addr(ids[1 - P.value], r + 1, vpool, ov);
-      softmax(r, [&](int h) {
-        // the scheduler keeps each pair of loads between the blocks of work
-        // around it
-        __builtin_amdgcn_sched_barrier(0);
-        if (h < 2) {
-          load_rows_s(sbk, ok[2 * h], Kn, 2 * h);
-          load_rows_s(sbk, ok[2 * h + 1], Kn, 2 * h + 1);
-        } else {
-          load_rows_s(sbv, ov[2 * h - 4], Vn, 2 * h - 4);
-          load_rows_s(sbv, ov[2 * h - 3], Vn, 2 * h - 3);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      });
+      uint32_t off[4];
+      const char *sb = step_addr(ids, r + 2, pool, off);
+      if (own) {
+        softmax(r, [&](int h) {
+          // the scheduler keeps each load between the blocks of work around it
+          __builtin_amdgcn_sched_barrier(0);
+          load_rows_s(sb, off[h], dst, h);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_rows_s(sb, off[i], dst, i);
+      }
     } else {
-      if (f_k) issue(ids[P.value], r + 2, kpool, Kn);
-      if (f_v) issue(ids[1 - P.value], r + 1, vpool, Vn);
-      softmax(r, [](int) {});
+      issue(ids, r + 2, pool, dst);
+      if (own) softmax(r, [](int) {});
     }
-
-    // the loads issued in the previous vector phase (read by the next matrix
-    // phase) have landed; this phase's may still be in flight.  (Nothing of
-    // the softmax is moved past the wait.)
+    // the loads of the previous vector phase (read from the next half-round on)
+    // have landed; this phase's may still be in flight.  (Nothing of the
+    // softmax is moved past the wait.)
     __builtin_amdgcn_sched_barrier(0);
-    if (BIGPAGE || f_k)
-      __builtin_amdgcn_s_waitcnt(ppair::vmcnt_imm(8));
-    else if (f_v)
-      __builtin_amdgcn_s_waitcnt(ppair::vmcnt_imm(4));
-    else
-      __builtin_amdgcn_s_waitcnt(ppair::vmcnt_imm(0));
-    // ids of step r+3, first read at the start of V(r+1)
-    if (f_ids) fetch_ids(ids[1 - P.value], kbeg + (r + 3) * BN);
+    __builtin_amdgcn_s_waitcnt(ppair::vmcnt_imm(4));
+    fetch_ids(ids, kbeg + (r + 3) * BN);
   };
 
-  // ---- rounds 0..T of this tile, two at a time so every buffer is a fixed
-  // array; then the output (outside the loop: the loop body stays small), then
-  // the barriers of the partner's remaining rounds
-  for (int r = 0; r <= T; r += 2) {
+  // ---- rounds 0..T, three at a time so every buffer is a fixed address; then
+  // the output
+  auto round = [&](int r, auto B) {
     if (GRP == 0) {
-      gphase(r, K0, V1);
+      gphase(r, B);
       __builtin_amdgcn_s_barrier();
-      vphase(r, std::integral_constant<int, 0>(), K0, V1);
+      vphase(r, B);
       __builtin_amdgcn_s_barrier();
     } else {
-      vphase(r - 1, std::integral_constant<int, 1>(), K1, V0);
+      vphase(r - 1, std::integral_constant<int, (B.value + 2) % 3>());
       __builtin_amdgcn_s_barrier();
-      gphase(r, K0, V1);
+      gphase(r, B);
       __builtin_amdgcn_s_barrier();
     }
+  };
+  for (int r = 0; r <= T; r += 3) {
+    round(r, std::integral_constant<int, 0>());
     if (r + 1 > T) break;
-    if (GRP == 0) {
-      gphase(r + 1, K1, V0);
-      __builtin_amdgcn_s_barrier();
-      vphase(r + 1, std::integral_constant<int, 1>(), K1, V0);
-      __builtin_amdgcn_s_barrier();
-    } else {
-      vphase(r, std::integral_constant<int, 0>(), K0, V1);
-      __builtin_amdgcn_s_barrier();
-      gphase(r + 1, K1, V0);
-      __builtin_amdgcn_s_barrier();
-    }
+    round(r + 1, std::integral_constant<int, 1>());
+    if (r + 2 > T) break;
+    round(r + 2, std::integral_constant<int, 2>());
   }
   __builtin_amdgcn_s_waitcnt(ppair::vmcnt_imm(0));  // no load may outlive the workgroup
-  epilogue();
-  for (int i = 0; i < 2 * (R - T); ++i) __builtin_amdgcn_s_barrier();
+  if (own) epilogue();
 }
 
 // One workgroup of 8 wavefronts: items 2*pair (wavefronts 0-3) and 2*pair+1
-// (wavefronts 4-7) of the list.
+// (wavefronts 4-7) of the list, siblings sharing one K/V stream.  A unit whose
+// first item is padding is skipped; an empty second item makes group 1 a
+// loader for group 0's tile.
 template <int PM>
 __device__ __forceinline__ void prefill_pair(const AttnArgs &a, int pair) {
+  using namespace ptile;
+  __shared__ __attribute__((aligned(1024))) unsigned char Kbuf[3 * BUFB], Vbuf[3 * BUFB];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i0 = 2 * pair, i1 = 2 * pair + 1;
   const Item it0 = a.items[i0];
+  if (it0.ntok == 0) return;
   Item it1 = it0;
   it1.ntok = 0;
-  if (i1 < a.n_items) it1 = a.items[i1];
-  auto steps = [](const Item &it) {
-    return it.ntok ? (it.kend - it.kbeg + ptile::BN - 1) / ptile::BN : 0;
-  };
-  const int T0 = steps(it0), T1 = steps(it1);
-  const int R = max(T0, T1);
-  if (R == 0) return;
+  if (i1 < a.n_items && a.items[i1].ntok > 0) it1 = a.items[i1];
+  const int kend_u = max(it0.kend, it1.kend);
+  const int T = (kend_u - it0.kbeg + BN - 1) / BN;
   if (wave < 4)
-    pair_group<PM, 0>(a, it0, T0, R, wave);
+    pair_group<PM, 0>(a, it0, it0.kbeg, kend_u, T, Kbuf, Vbuf, wave);
   else
-    pair_group<PM, 1>(a, it1, T1, R, wave - 4);
+    pair_group<PM, 1>(a, it1, it0.kbeg, kend_u, T, Kbuf, Vbuf, wave - 4);
 }
 
 }  // namespace rpkv

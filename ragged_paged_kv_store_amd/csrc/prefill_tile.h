@@ -239,8 +239,12 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      if (st + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      // each K read right after the MFMA that consumed the register it refills
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (st + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
       if (st & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
 
@@ -300,13 +304,18 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
           o[db] = mfma32(vf, pf[kb][s2], o[db]);
           if (db == 3) load_rows(vsrc[2 * kb + s2], Vn, 2 * kb + s2);
         }
-    // transposing reads one 16-key block ahead of its 4 MFMAs, a V load after
-    // each block (0x100: LDS reads, 0x8: MFMA, 0x20: memory reads)
+    // transposing reads one 16-key block ahead: the two reads of the next
+    // block's fragment db right after the MFMA that consumed this block's
+    // fragment db; a V load after each block (0x100: LDS reads, 0x8: MFMA,
+    // 0x20: memory reads)
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
-      if (blk + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if (blk + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
     }
 

@@ -66,8 +66,8 @@ struct CascNode {
 // faults on every plan).
 struct PlanScratch {
   std::vector<Item> tiles, pre, dec, dlast;
-  std::vector<int64_t> tile_key, pre_key;
-  std::vector<int32_t> nsplit, deepest, runs;
+  std::vector<int64_t> tile_key, pre_key, work, ukey;
+  std::vector<int32_t> nsplit, deepest, runs, order, idx, first, second;
 };
 
 struct HostPlan {

@@ -126,6 +126,18 @@ bool check_partition(const Batch &b, const rpkv::Shape &s, const rpkv::HostPlan 
               "token %d: merge record", t);
       }
     }
+  // two tiles per workgroup: siblings sharing one K/V stream, padding never first
+  if (hp.tiles_per_block == 2) {
+    CHECK(hp.prefill.size() % 16 == 0, "pair list not a whole number of XCD rounds");
+    for (size_t k = 0; k + 1 < hp.prefill.size(); k += 2) {
+      const rpkv::Item &x = hp.prefill[k], &y = hp.prefill[k + 1];
+      if (y.ntok == 0) continue;
+      CHECK(x.ntok > 0, "workgroup %zu: padding before a tile", k / 2);
+      CHECK(x.req == y.req && x.kvh == y.kvh && x.kbeg == y.kbeg && (x.pos0 < 0) == (y.pos0 < 0) &&
+                (x.pos0 >= 0 || x.kend == y.kend),
+            "workgroup %zu: tiles that do not share K/V", k / 2);
+    }
+  }
   const rpkv::MetaLayout need = rpkv::meta_layout(rpkv::meta_counts(hp, s.max_batch));
   const rpkv::MetaLayout cap = rpkv::meta_layout(rpkv::meta_caps(s));
   CHECK(need.bytes <= cap.bytes, "metadata %zu bytes > capacity %zu", need.bytes, cap.bytes);

@@ -254,6 +254,8 @@ def test_random_batches_covered_exactly_once(rp, seed):
     if dtype == "bf16" and kw["tiles_per_block"]:
         assert p.info()["tiles_per_block"] == kw["tiles_per_block"]
         assert len(p.items(0)) % (8 * kw["tiles_per_block"]) == 0
+    if p.info()["tiles_per_block"] == 2:
+        check_sibling_pairs(p)
 
 
 def test_full_config_plans(rp):
@@ -272,6 +274,24 @@ def test_full_config_plans(rp):
     assert info["plan_host_us"] < 50_000
 
 
+def check_sibling_pairs(plan):
+    """With two tiles per workgroup, the tiles of a workgroup share one K/V
+    stream: the second (when present) has the first's request, KV head and
+    first key (and, for cascade level tiles, last key); padding never comes
+    first."""
+    items = plan.items(0)
+    assert len(items) % 16 == 0
+    for p in range(len(items) // 2):
+        a, b = items[2 * p], items[2 * p + 1]
+        if b[3] == 0:
+            continue
+        assert a[3] > 0, p
+        assert (a[0], a[1], a[5]) == (b[0], b[1], b[5]), (p, a, b)
+        assert (a[4] < 0) == (b[4] < 0), (p, a, b)
+        if a[4] < 0:
+            assert a[6] == b[6], (p, a, b)
+
+
 def test_tiles_per_block_choice_and_pair_layout(rp):
     """The planner runs MFMA tiles in pairs (two per 8-wavefront workgroup, in
     ping-pong) when the batch's tiles average at least 24 steps of 64 keys, else
@@ -283,6 +303,8 @@ def test_tiles_per_block_choice_and_pair_layout(rp):
         p = make_plan(rp, spec)
         p.plan_host(spec.cu_q, spec.L, spec.page_table.shape[1], spec.page_table, spec.groups)
         assert p.info()["tiles_per_block"] == want, cid
+        if want == 2:
+            check_sibling_pairs(p)
     for cid in (2, 4):
         spec = synth.small_config(cid)
         for tpb in (1, 2):
@@ -291,6 +313,8 @@ def test_tiles_per_block_choice_and_pair_layout(rp):
             assert p.info()["tiles_per_block"] == tpb
             assert len(p.items(0)) % (8 * tpb) == 0
             check_coverage(rp, p, spec)
+            if tpb == 2:
+                check_sibling_pairs(p)
     ok, _ = rp.supports(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, dtype=0,
                         max_batch=4, num_pages=64, max_tokens=64, max_pages_per_req=8,
                         tiles_per_block=3)
