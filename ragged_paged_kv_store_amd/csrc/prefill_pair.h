@@ -1,7 +1,8 @@
 // bf16 MFMA attention tiles, two per workgroup in ping-pong, sharing K/V.
 //
 // A workgroup of 8 wavefronts runs two tiles (items 2p and 2p+1 of the prefill
-// list), one per group of 4 wavefronts; wavefronts w and w+4 share a SIMD.  The
+// list), one per group of 4 wavefronts (group 0 on wavefronts 4-7, group 1 on
+// 0-3); wavefronts w and w+4 share a SIMD.  The
 // two tiles are siblings: query rows of the same request and KV head over the
 // same first key (adjacent row blocks of one causal chunk, or of one cascade
 // level chunk), so one stream of K/V rows staged in LDS serves both; the planner
@@ -232,6 +233,10 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
   // LDS address is a fixed offset)
   auto gphase = [&](int r, auto B) {
     if (!own || r > T) return;
+    // the wavefront issuing MFMAs goes first when its SIMD partner (in its
+    // vector phase) also has an instruction ready
+    __builtin_amdgcn_s_setprio(3);
+    __builtin_amdgcn_sched_barrier(0);
     const unsigned char *Kb = Kbuf + B.value * BUFB;
     const unsigned char *Vp = Vbuf + ((B.value + 2) % 3) * BUFB;  // V(r-1)
     if (r < T) {
@@ -294,6 +299,8 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
           if (blk + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   auto epilogue = [&]() {
@@ -444,10 +451,12 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
   if (own) epilogue();
 }
 
-// One workgroup of 8 wavefronts: items 2*pair (wavefronts 0-3) and 2*pair+1
-// (wavefronts 4-7) of the list, siblings sharing one K/V stream.  A unit whose
-// first item is padding is skipped; an empty second item makes group 1 a
-// loader for group 0's tile.
+// One workgroup of 8 wavefronts: items 2*pair (group 0, on wavefronts 4-7) and
+// 2*pair+1 (group 1, on wavefronts 0-3) of the list, siblings sharing one K/V
+// stream.  (Group 0 runs its matrix phase first; on the younger wavefronts it
+// balances the two half-rounds better: an SIMD's older wavefront wins issue
+// when both have an instruction ready.)  A unit whose first item is padding is
+// skipped; an empty second item makes group 1 a loader for group 0's tile.
 template <int PM>
 __device__ __forceinline__ void prefill_pair(const AttnArgs &a, int pair) {
   using namespace ptile;
@@ -461,10 +470,10 @@ __device__ __forceinline__ void prefill_pair(const AttnArgs &a, int pair) {
   if (i1 < a.n_items && a.items[i1].ntok > 0) it1 = a.items[i1];
   const int kend_u = max(it0.kend, it1.kend);
   const int T = (kend_u - it0.kbeg + BN - 1) / BN;
-  if (wave < 4)
-    pair_group<PM, 0>(a, it0, it0.kbeg, kend_u, T, Kbuf, Vbuf, wave);
+  if (wave >= 4)
+    pair_group<PM, 0>(a, it0, it0.kbeg, kend_u, T, Kbuf, Vbuf, wave - 4);
   else
-    pair_group<PM, 1>(a, it1, it0.kbeg, kend_u, T, Kbuf, Vbuf, wave - 4);
+    pair_group<PM, 1>(a, it1, it0.kbeg, kend_u, T, Kbuf, Vbuf, wave);
 }
 
 }  // namespace rpkv
