@@ -158,10 +158,12 @@ def metadata_build_us(spec, db, rp, torch, reps: int = 50):
     return {"device": round(dev_us, 2), "host_numpy": round(host_us, 2)}
 
 
-def cpu_baseline(spec, db, H, budget_flops: float = 40e9):
+def cpu_baseline(spec, db, H, budget_flops: float = 80e9):
     """The fp64 oracle as it stands, on the host, over one layer of the batch:
-    every row when the layer is within ~40 GFLOP (about 30 core-seconds),
-    otherwise a seeded sample of requests and rows within that budget."""
+    every row when the layer is within ~80 GFLOP (about 30 core-seconds),
+    otherwise a seeded sample of requests and rows within that budget, taken in
+    runs of consecutive rows (the oracle deals consecutive tokens to its
+    threads, so a run keeps every thread busy)."""
     import oracle
     from tests import gpu_harness as GH
     rng = np.random.default_rng(0)
@@ -177,21 +179,23 @@ def cpu_baseline(spec, db, H, budget_flops: float = 40e9):
     else:
         reqs = GH.pick_requests(spec, rng, max_reqs=16)
         sub = GH.subproblem(spec, db, reqs)
-        rows = GH.pick_rows(spec, reqs, rng, per_req=4)[sub.token_map]
         s = sub.spec
         cu = s.cu_q
-        # trim to the budget, keeping the first rows picked of each request
+        rows = np.zeros(s.T, bool)
         acc = 0
-        for i in range(s.bs):
-            for r in range(int(s.n[i])):
-                if rows[cu[i] + r]:
-                    f = 4 * s.D * s.Hq * (int(s.L[i]) - int(s.n[i]) + r + 1)
-                    if acc + f > budget_flops and acc > 0:
-                        rows[cu[i] + r] = False
-                    else:
-                        acc += f
-        sample = (f"seeded sample: {int(rows.sum())} rows x {spec.Hq} heads of {len(reqs)} "
-                  f"requests")
+        used = 0
+        for i in rng.permutation(s.bs):
+            ni, Li = int(s.n[i]), int(s.L[i])
+            run = min(ni, cores)
+            r0 = int(rng.integers(0, ni - run + 1))
+            f = sum(4 * s.D * s.Hq * (Li - ni + r + 1) for r in range(r0, r0 + run))
+            if acc + f > budget_flops and acc > 0:
+                continue
+            rows[cu[i] + r0:cu[i] + r0 + run] = True
+            acc += f
+            used += 1
+        sample = (f"seeded sample: {int(rows.sum())} rows x {spec.Hq} heads of {used} requests, "
+                  f"in runs of up to {cores} consecutive rows")
     s = sub.spec
     t0 = time.perf_counter()
     oracle.store_then_attend(s, sub.tensors, rows=rows, nthreads=cores)
