@@ -17,7 +17,11 @@
 // tile (prefill_tile.h); only the schedule differs.  With half-round h:
 //   round r, group 0:  G(r) [h = 2r]   | V(r)   [h = 2r+1]
 //            group 1:  V(r-1) [h = 2r] | G(r)   [h = 2r+1]
-//   G(r): S(r) from K(r), then O += P(r-1) V(r-1)
+//   G(r): S(r) from K(r) and O += P(r-1) V(r-1), interleaved (two 16-channel
+//         slices of S, then one 16-key block of PV, four times), so the
+//         transposing V reads spread over the phase instead of following
+//         the K reads; round 0 multiplies a zeroed V buffer by P = 0 and
+//         round T's S is discarded, so every round runs the same code
 //   V(r): softmax of S(r) into P(r); group 0 loads K(r+2), group 1 loads
 //         V(r+2) (four 1 KiB loads per wavefront); then the wait for the loads
 //         this group issued in its previous vector phase.
@@ -38,6 +42,7 @@ namespace rpkv {
 
 namespace ppair {
 // s_waitcnt immediate for "vector memory count <= n", other counters untouched
+// (clear bits 8-11 as well to wait for LDS and scalar memory too)
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 }  // namespace ppair
 
@@ -198,7 +203,15 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
   const int vc0 = 2 * (vg & 1) + (vq >> 1);
 
   f32x16 s[2];
+  // P(r-1) of the PV product; zero before the first step (the first matrix
+  // phase's PV then adds nothing)
   bf16x8 pf[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pf[kb][s2][i] = (__bf16)0.f;
   // this group's share of the loads: K rows (group 0) or V rows (group 1) of
   // each step, rows 16*lw.. of the buffer of the step
   const char *pool = GRP == 0 ? kpool : vpool;
@@ -224,7 +237,16 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
 #pragma unroll
       for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*(const u32x4 *)(qrow + 16 * s + 8 * half));
     }
-    __builtin_amdgcn_s_waitcnt(ppair::vmcnt_imm(0));
+    // V(-1): buffer 2, read (with zero weights) in round 0, must hold finite
+    // values: 8 wavefronts x 2 x 1 KiB of zeros
+    {
+      const int w8 = GRP == 0 ? 4 + lw : lw;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        *(u32x4 *)(Vbuf + 2 * BUFB + (w8 * 2 + i) * 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+    }
+    // (the zeros and every load have landed before the barrier)
+    __builtin_amdgcn_s_waitcnt(ppair::vmcnt_imm(0) & ~(15 << 8));
   }
   __builtin_amdgcn_s_barrier();
 
@@ -239,66 +261,73 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
     __builtin_amdgcn_sched_barrier(0);
     const unsigned char *Kb = Kbuf + B.value * BUFB;
     const unsigned char *Vp = Vbuf + ((B.value + 2) % 3) * BUFB;  // V(r-1)
-    if (r < T) {
+    // S(r) = K(r) Q^T in four pairs of 16-channel slices, each followed by one
+    // 16-key block of O += P(r-1) V(r-1): every 8 MFMAs carry 4 K reads and 8
+    // transposing V reads, so LDS work is spread evenly over the phase.  (Round
+    // 0 adds P = 0 times a zeroed V buffer; round T's S is not used.)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    auto kread = [&](int st, bf16x8(&dst)[2]) {
+      const int ch = (2 * st + half) ^ kx;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
+        dst[kb] = as_bf16x8(*(const u32x4 *)(Kb + (kb * 32 + q32) * ROWB + 16 * ch));
+    };
+    auto vread = [&](int blk, bf16x8(&dst)[4]) {
+      const int kb = blk >> 1, s2 = blk & 1;
+      const unsigned char *rp = Vp + (vrow + 16 * s2 + 32 * kb) * ROWB + 8 * (vq & 1);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-      bf16x8 kf[3][2];
-      auto kread = [&](int st, bf16x8(&dst)[2]) {
-        const int ch = (2 * st + half) ^ kx;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          dst[kb] = as_bf16x8(*(const u32x4 *)(Kb + (kb * 32 + q32) * ROWB + 16 * ch));
-      };
-      kread(0, kf[0]);
-      kread(1, kf[1]);
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        if (st + 2 < 8) kread(st + 2, kf[(st + 2) % 3]);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kf[st % 3][kb], qf[st], s[kb]);
+      for (int db = 0; db < 4; ++db) {
+        const v4i16 lo = tr_read(rp + 16 * ((vc0 + 4 * db) ^ vx));
+        const v4i16 hi = tr_read(rp + 8 * ROWB + 16 * ((vc0 + 4 * db) ^ vx ^ 1));
+        dst[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-      // each K read right after the MFMA that consumed the register it refills
-      // (0x100: LDS reads, 0x8: MFMA)
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    };
+    bf16x8 kf[2][2], vf[4];
+    kread(0, kf[0]);
+    kread(1, kf[1]);
 #pragma unroll
-      for (int st = 0; st < 8; ++st)
+    for (int u = 0; u < 4; ++u) {
+      vread(u, vf);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (st + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      // the products stay in this phase
-      asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kf[h][kb], qf[2 * u + h], s[kb]);
+      if (u < 3) {
+        // (written last-needed first: the scheduler places them in reverse)
+        auto kread_rev = [&](int st, bf16x8(&dst)[2]) {
+          const int ch = (2 * st + half) ^ kx;
+#pragma unroll
+          for (int kb = 1; kb >= 0; --kb)
+            dst[kb] = as_bf16x8(*(const u32x4 *)(Kb + (kb * 32 + q32) * ROWB + 16 * ch));
+        };
+        kread_rev(2 * u + 3, kf[1]);
+        kread_rev(2 * u + 2, kf[0]);
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = mfma32(vf[db], pf[u >> 1][u & 1], o[db]);
     }
-    if (r >= 1) {
+    // order: the first pair's K reads; then per unit, the S MFMAs with the
+    // unit's V reads two after each, the PV MFMAs with the next pair's K reads
+    // one after each (0x100: LDS reads, 0x8: MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
 #pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const unsigned char *rp = Vp + (vrow + 16 * s2 + 32 * kb) * ROWB + 8 * (vq & 1);
-            const v4i16 lo = tr_read(rp + 16 * ((vc0 + 4 * db) ^ vx));
-            const v4i16 hi = tr_read(rp + 8 * ROWB + 16 * ((vc0 + 4 * db) ^ vx ^ 1));
-            const bf16x8 vf = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[db] = mfma32(vf, pf[kb][s2], o[db]);
-          }
-      // the two transposing reads of the next block's V^T fragment db right after
-      // the MFMA that consumed this block's fragment db: each read has the
-      // remaining three MFMAs of the block to land, and the wavefront never
-      // issues a run of MFMAs with no reads of the next block in flight
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-          if (blk + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-        }
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (u < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
+    // the products stay in this phase
+    asm volatile("" : "+v"(s[0]), "+v"(s[1]));
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
   };
@@ -376,15 +405,23 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
         for (int j = 0; j < 4; ++j) {
           const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * s2 + 2 * j], c, -mu));
           const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * s2 + 2 * j + 1], c, -mu));
-          const bf16x2 pp = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-          float &acc = (j & 1) ? sum1 : sum0;
-          acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
-          w[j] = __builtin_bit_cast(uint32_t, pp);
+          w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
         }
-        pf[kb][s2] = as_bf16x8(w);
         // computed here, not sunk toward its use in the next matrix phase
         // (past the barrier)
+        pf[kb][s2] = as_bf16x8(w);
         asm volatile("" : "+v"(pf[kb][s2]));
+        // the sums read the finished P registers, so the packed words need no
+        // second home.  (Operands taken as shuffles of the bf16 vector: taken
+        // as bit-cast 32-bit lanes of it, the compiler fed one lane to two
+        // dot products.)
+        {
+          const bf16x8 pv = pf[kb][s2];
+          sum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 0, 1), ones, sum0, false);
+          sum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), ones, sum1, false);
+          sum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), ones, sum0, false);
+          sum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), ones, sum1, false);
+        }
         if (2 * kb + s2 < 3) hook(2 * kb + s2 + 1);
       }
     lrun += sum0 + sum1;
