@@ -257,12 +257,14 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
         for (int i = 0; i < 16; ++i)
           s[kb][i] = (32 * kb + (i >> 2) * 8 + (i & 3)) <= rel ? s[kb][i] : kNegInf;
     }
-    float mx = kNegInf;
+    // one 3-input max per two logits, in two independent chains
+    float mx0 = kNegInf, mx1 = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
-    mx = max_halves(mx) * c;
+    for (int i = 0; i < 16; i += 2) {
+      mx0 = fmaxf(fmaxf(mx0, s[0][i]), s[0][i + 1]);
+      mx1 = fmaxf(fmaxf(mx1, s[1][i]), s[1][i + 1]);
+    }
+    float mx = max_halves(fmaxf(mx0, mx1)) * c;
     if (mx > mref + 8.f) {
       const float al = fast_exp2(mref - mx);  // 0 on the first update
       lrun *= al;
@@ -271,7 +273,12 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
       for (int db = 0; db < 4; ++db) o[db] = o[db] * al;
     }
     const float mu = mref == kNegInf ? 0.f : mref;
-    float sum = 0.f;
+    // the row sum adds the bf16 weights the PV product uses, two per instruction
+    // (v_dot2 against (1, 1): exact products, fp32 sums), reading each finished
+    // P fragment (its bf16 pairs taken as shuffles of the vector: as bit-cast
+    // 32-bit lanes the compiler has fed one lane to two dot products)
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float sum0 = 0.f, sum1 = 0.f;
     bf16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -282,12 +289,17 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
         for (int j = 0; j < 4; ++j) {
           const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * s2 + 2 * j], c, -mu));
           const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * s2 + 2 * j + 1], c, -mu));
-          sum += p0 + p1;
           w[j] = pack_bf16x2(p0, p1);
         }
         pf[kb][s2] = as_bf16x8(w);
+        asm volatile("" : "+v"(pf[kb][s2]));
+        const bf16x8 pv = pf[kb][s2];
+        sum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 0, 1), ones, sum0, false);
+        sum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), ones, sum1, false);
+        sum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), ones, sum0, false);
+        sum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), ones, sum1, false);
       }
-    lrun += sum;
+    lrun += sum0 + sum1;
 
     // ---- O^T += V^T P^T (V^T through the transposing LDS read)
 #pragma unroll
