@@ -306,6 +306,17 @@ rpkv_status rpkv_last_indices(const rpkv_plan *plan, int32_t *out_host);
 /* Summary of the last planned batch. */
 rpkv_status rpkv_plan_get_info(const rpkv_plan *plan, rpkv_plan_info *info);
 
+/* One-line text summary of the last planned batch, for logs (mini-sglang
+ * "Creating a backend: one or a pair" logs the backend a run uses; here the
+ * choice is per batch): request classes, MFMA tiles and tiles per workgroup,
+ * split-KV chunks and their length, cascade levels, partials and merged tokens,
+ * metadata bytes and host planning time.  Writes at most size bytes into buf,
+ * always NUL-terminated (truncated if short; 512 bytes always suffice).
+ * NOT_PREPARED before the first successful plan.  With the environment variable
+ * RPKV_LOG_PLANS set (and not "0") when the library first plans, every
+ * successful plan prints this line to stderr, prefixed "rpkv: ". */
+rpkv_status rpkv_plan_summary(const rpkv_plan *plan, char *buf, size_t size);
+
 /* Host copy of the last plan's work items for inspection: kind 0 = prefill
  * tiles, 1 = decode chunks.  Each item is 8 int32: request, KV head, first
  * token (or cascade token-list offset), token count, position of the first

@@ -35,7 +35,7 @@ EXPORTS = (
     "rpkv_store_kv", "rpkv_attend", "rpkv_forward", "rpkv_timing_enable", "rpkv_timing_collect",
     "rpkv_build_metadata", "rpkv_graph_decode_init", "rpkv_graph_decode_forward",
     "rpkv_prepare_metadata_csr", "rpkv_rewrite_block_table", "rpkv_plan_get_cascade_tree",
-    "rpkv_check_slot_mapping", "rpkv_graph_decode_forward_noalloc",
+    "rpkv_check_slot_mapping", "rpkv_graph_decode_forward_noalloc", "rpkv_plan_summary",
 )
 
 
@@ -114,6 +114,7 @@ def _load():
         "rpkv_graph_decode_forward": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp,
                                             ctypes.c_float, vp]),
         "rpkv_check_slot_mapping": (i32, [vp, vp, i64]),
+        "rpkv_plan_summary": (i32, [vp, ctypes.c_char_p, sz]),
         "rpkv_graph_decode_forward_noalloc": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                                     vp, i64, i32, vp, ctypes.c_float, vp]),
     }
@@ -381,6 +382,12 @@ class Plan:
         inf = PlanInfo()
         _check(lib.rpkv_plan_get_info(self._h, ctypes.byref(inf)))
         return inf.as_dict()
+
+    def summary(self) -> str:
+        """One-line text summary of the last planned batch (rpkv_plan_summary)."""
+        buf = ctypes.create_string_buffer(512)
+        _check(lib.rpkv_plan_summary(self._h, buf, ctypes.sizeof(buf)))
+        return buf.value.decode()
 
     def items(self, kind: int) -> np.ndarray:
         n = ctypes.c_int32()

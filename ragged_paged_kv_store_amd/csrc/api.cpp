@@ -3,6 +3,8 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -15,6 +17,16 @@ using rpkv::Item;
 using rpkv::Shape;
 
 namespace {
+
+// Opt-in plan log: RPKV_LOG_PLANS set to anything but "0" prints each
+// successful plan's summary line to stderr.
+bool log_plans() {
+  static const bool on = [] {
+    const char *v = std::getenv("RPKV_LOG_PLANS");
+    return v && *v && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
 thread_local std::string g_err;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -140,6 +152,36 @@ rpkv_status rpkv_plan_batch(rpkv_plan *p, int32_t batch, const int32_t *cu, cons
   p->lay = lay;
   p->planned = true;
   p->ws_need = workspace_need(p);
+  if (log_plans()) {
+    char line[512];
+    if (rpkv_plan_summary(p, line, sizeof line) == RPKV_OK) std::fprintf(stderr, "rpkv: %s\n", line);
+  }
+  return RPKV_OK;
+}
+
+rpkv_status rpkv_plan_summary(const rpkv_plan *p, char *buf, size_t size) {
+  if (!p || !buf || size == 0) return fail(RPKV_ERR_INVALID_ARG, "plan or buffer is NULL or empty");
+  if (!p->planned) return fail(RPKV_ERR_NOT_PREPARED, "no planned batch");
+  const HostPlan &hp = p->hp;
+  int32_t ndec_req = 0, npre_req = 0, nempty = 0;
+  for (int32_t i = 0; i < hp.batch; ++i) {
+    const int32_t n = hp.cu_q[i + 1] - hp.cu_q[i];
+    if (n == 0) ++nempty;
+    else if ((int64_t)n * p->s.G() <= p->s.decode_max_rows) ++ndec_req;
+    else ++npre_req;
+  }
+  int64_t nm = 0;
+  for (const rpkv::CascNode &nd : hp.tree) nm += (int64_t)nd.members.size();
+  std::snprintf(buf, size,
+                "batch %d (%d tokens): %d decode-type, %d prefill-type, %d empty requests; "
+                "%d MFMA tiles (%d per workgroup, %d in shared-prefix levels), %zu split-KV "
+                "chunks of %d keys; %zu cascade levels (depth %d, %lld member entries, %d "
+                "requests); %lld partials, %zu tokens merged; metadata %zu bytes; planned "
+                "in %.1f us",
+                hp.batch, hp.T, ndec_req, npre_req, nempty, hp.n_prefill_real, hp.tiles_per_block,
+                hp.n_cascade_items, hp.decode.size(), hp.decode_chunk, hp.tree.size(),
+                hp.cascade_depth, (long long)nm, hp.cascade_members, (long long)hp.n_partials,
+                hp.merge.size() / 3, p->lay.bytes, hp.plan_us);
   return RPKV_OK;
 }
 
