@@ -332,22 +332,45 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
     __builtin_amdgcn_s_setprio(0);
   };
 
+  // The output rows leave through LDS: each wavefront writes its 32 rows there
+  // (row stride padded by 16 bytes against bank conflicts), then stores whole
+  // 256-byte rows, 16 lanes per row and four rows per instruction.  (Stored
+  // straight from the accumulators, every instruction wrote 16-byte pieces of
+  // 32 rows, and a workgroup retires only once its stores are acknowledged:
+  // C4's launch took 3% longer.)  The K/V buffers are free by then.
   auto epilogue = [&]() {
     float l = sum_halves(lrun);
-    if (!rowv) return;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (it.split < 0) {
-      uint16_t *orow = (uint16_t *)a.out + ((int64_t)tok * a.Hq + qh) * D;
+      constexpr int SROW = ROWB + 16;
+      unsigned char *stg = (GRP == 0 ? Kbuf : Vbuf) + lw * (32 * SROW);
+      if (rowv) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          u32x2 w;
-          w[0] = pack_bf16x2(o[db][4 * g4 + 0] * inv, o[db][4 * g4 + 1] * inv);
-          w[1] = pack_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv);
-          *(u32x2 *)(orow + 32 * db + 8 * g4 + 4 * half) = w;
+          for (int g4 = 0; g4 < 4; ++g4) {
+            u32x2 w;
+            w[0] = pack_bf16x2(o[db][4 * g4 + 0] * inv, o[db][4 * g4 + 1] * inv);
+            w[1] = pack_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv);
+            *(u32x2 *)(stg + q32 * SROW + 2 * (32 * db + 8 * g4 + 4 * half)) = w;
+          }
+      }
+      // the global row of each of the wavefront's rows, from the lane holding it
+      const int64_t grow = (int64_t)tok * a.Hq + qh;
+      const int32_t glo = (int32_t)grow, ghi = (int32_t)(grow >> 32);
+      const int c16 = lane & 15, rsub = lane >> 4;
+      unsigned char *out = (unsigned char *)a.out;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = 4 * k + rsub;
+        const int64_t gr = ((int64_t)__shfl(ghi, r, 64) << 32) | (uint32_t)__shfl(glo, r, 64);
+        if (lw * 32 + r < rows) {
+          const u32x4 v = *(const u32x4 *)(stg + r * SROW + 16 * c16);
+          *(u32x4 *)(out + gr * (D * 2) + 16 * c16) = v;
         }
+      }
     } else {
+      if (!rowv) return;
       const int64_t pi = (int64_t)pbase + it.split;
       float *prow = a.o_part + (pi * a.Hq + qh) * D;
 #pragma unroll
@@ -485,6 +508,9 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
     round(r + 2, std::integral_constant<int, 2>());
   }
   __builtin_amdgcn_s_waitcnt(ppair::vmcnt_imm(0));  // no load may outlive the workgroup
+  // every wavefront's loads have landed and its LDS reads are done (the fences
+  // wait for them): the epilogue may write into the buffers
+  __syncthreads();
   if (own) epilogue();
 }
 
