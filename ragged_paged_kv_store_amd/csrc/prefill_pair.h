@@ -13,8 +13,10 @@
 // these phases in opposite order, separated by workgroup barriers, so on every
 // SIMD one wavefront issues MFMAs while its partner does the softmax.
 //
-// Tile layout, masking, softmax and operand formats are those of the 4-wavefront
-// tile (prefill_tile.h); only the schedule differs.  With half-round h:
+// Tile layout, masking and operand formats are those of the 4-wavefront tile
+// (prefill_tile.h), and so is the softmax except for its reference (the row max
+// of the first step only; see prefill_pair below); the schedule differs.  With
+// half-round h:
 //   round r, group 0:  G(r) [h = 2r]   | V(r)   [h = 2r+1]
 //            group 1:  V(r-1) [h = 2r] | G(r)   [h = 2r+1]
 //   G(r): S(r) from K(r) and O += P(r-1) V(r-1), interleaved (two 16-channel
@@ -46,10 +48,10 @@ namespace ppair {
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 }  // namespace ppair
 
-template <int PM, int GRP>
-__device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, const int kbeg,
+template <int PM, int GRP, bool EXACT>
+__device__ __forceinline__ bool pair_group(const AttnArgs &a, const Item &it, const int kbeg,
                                            const int kend_u, const int T, unsigned char *Kbuf,
-                                           unsigned char *Vbuf, const int lw) {
+                                           unsigned char *Vbuf, const int lw, int *redo) {
   using namespace ptile;
   constexpr bool BIGPAGE = PM == 2;
   const bool own = it.ntok > 0;  // false: this group only loads (no tile)
@@ -399,20 +401,22 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
           s[kb][i] = (32 * kb + (i >> 2) * 8 + (i & 3)) <= rel ? s[kb][i] : kNegInf;
     }
     hook(0);
-    // one 3-input max per two logits, in two independent chains
-    float mx0 = kNegInf, mx1 = kNegInf;
+    if (EXACT || r == 0) {
+      // one 3-input max per two logits, in two independent chains
+      float mx0 = kNegInf, mx1 = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      mx0 = fmaxf(fmaxf(mx0, s[0][i]), s[0][i + 1]);
-      mx1 = fmaxf(fmaxf(mx1, s[1][i]), s[1][i + 1]);
-    }
-    float mx = max_halves(fmaxf(mx0, mx1)) * c;
-    if (mx > mref + 8.f) {
-      const float al = fast_exp2(mref - mx);
-      lrun *= al;
-      mref = mx;
+      for (int i = 0; i < 16; i += 2) {
+        mx0 = fmaxf(fmaxf(mx0, s[0][i]), s[0][i + 1]);
+        mx1 = fmaxf(fmaxf(mx1, s[1][i]), s[1][i + 1]);
+      }
+      const float mx = max_halves(fmaxf(mx0, mx1)) * c;
+      if (mx > mref + 8.f) {
+        const float al = fast_exp2(mref - mx);
+        lrun *= al;
+        mref = mx;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = o[db] * al;
+        for (int db = 0; db < 4; ++db) o[db] = o[db] * al;
+      }
     }
     const float mu = mref == kNegInf ? 0.f : mref;
     // the row sum adds the bf16 weights the PV product uses, two per
@@ -509,9 +513,17 @@ __device__ __forceinline__ void pair_group(const AttnArgs &a, const Item &it, co
   }
   __builtin_amdgcn_s_waitcnt(ppair::vmcnt_imm(0));  // no load may outlive the workgroup
   // every wavefront's loads have landed and its LDS reads are done (the fences
-  // wait for them): the epilogue may write into the buffers
+  // wait for them): the buffers may be written again
   __syncthreads();
+  if (!EXACT) {
+    // a weight sum at or above 2^64, inf or NaN asks for the second pass (bit
+    // patterns of non-negative floats order as integers)
+    if (own && __any(__builtin_bit_cast(uint32_t, lrun) >= 0x5f800000u) && lane == 0) *redo = 1;
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(*(volatile int *)redo) != 0) return true;
+  }
   if (own) epilogue();
+  return false;
 }
 
 // One workgroup of 8 wavefronts: items 2*pair (group 0, on wavefronts 4-7) and
@@ -524,6 +536,7 @@ template <int PM>
 __device__ __forceinline__ void prefill_pair(const AttnArgs &a, int pair) {
   using namespace ptile;
   __shared__ __attribute__((aligned(1024))) unsigned char Kbuf[3 * BUFB], Vbuf[3 * BUFB];
+  __shared__ int redo;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i0 = 2 * pair, i1 = 2 * pair + 1;
   const Item it0 = a.items[i0];
@@ -533,10 +546,41 @@ __device__ __forceinline__ void prefill_pair(const AttnArgs &a, int pair) {
   if (i1 < a.n_items && a.items[i1].ntok > 0) it1 = a.items[i1];
   const int kend_u = max(it0.kend, it1.kend);
   const int T = (kend_u - it0.kbeg + BN - 1) / BN;
-  if (wave >= 4)
-    pair_group<PM, 0>(a, it0, it0.kbeg, kend_u, T, Kbuf, Vbuf, wave - 4);
-  else
-    pair_group<PM, 1>(a, it1, it0.kbeg, kend_u, T, Kbuf, Vbuf, wave);
+  if (threadIdx.x == 0) redo = 0;  // published by the groups' first barrier
+  // First pass: each row's weights are taken against its max over the tile's
+  // first step, and later steps take no row max at all (the softmax does not
+  // depend on the reference; only the range of the weights does).  A weight
+  // exceeds 1 where a later logit exceeds that max, and is at most the row's
+  // weight sum; while every sum stays below 2^64 no weight, sum or output can
+  // overflow (for values of V below 2^60).  Otherwise the workgroup runs its
+  // tiles again with the running max of every step (second pass, EXACT).
+  const bool again = wave >= 4 ? pair_group<PM, 0, false>(a, it0, it0.kbeg, kend_u, T, Kbuf, Vbuf, wave - 4, &redo)
+                                : pair_group<PM, 1, false>(a, it1, it0.kbeg, kend_u, T, Kbuf, Vbuf, wave, &redo);
+  if (again) {
+    // the items read afresh (the values of the first pass are not kept for
+    // this one), made uniform again field by field
+    auto item_at = [&](int i) {
+      const int32_t *src = (const int32_t *)(a.items + i);
+      Item v;
+      int32_t *dst = (int32_t *)&v;
+#pragma unroll
+      for (int f = 0; f < 8; ++f) dst[f] = __builtin_amdgcn_readfirstlane(((const volatile int32_t *)src)[f]);
+      return v;
+    };
+    const Item r0 = item_at(i0);
+    Item r1 = r0;
+    r1.ntok = 0;
+    if (i1 < a.n_items) {
+      const Item t1 = item_at(i1);
+      if (t1.ntok > 0) r1 = t1;
+    }
+    const int ke = max(r0.kend, r1.kend);
+    const int Tr = (ke - r0.kbeg + BN - 1) / BN;
+    if (wave >= 4)
+      pair_group<PM, 0, true>(a, r0, r0.kbeg, ke, Tr, Kbuf, Vbuf, wave - 4, &redo);
+    else
+      pair_group<PM, 1, true>(a, r1, r0.kbeg, ke, Tr, Kbuf, Vbuf, wave, &redo);
+  }
 }
 
 }  // namespace rpkv

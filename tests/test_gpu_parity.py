@@ -154,18 +154,23 @@ def _ramp(spec, ht, reverse=False):
         ht.k[cu[i]:cu[i + 1]] = synth.f32_to_bf16_bits(-K if reverse else K)
 
 
+@pytest.mark.parametrize("tpb", [1, 2])
 @pytest.mark.parametrize("reverse", [False, True])
-def test_ramp_probe_pins_mask_boundary(reverse):
+def test_ramp_probe_pins_mask_boundary(reverse, tpb):
     """Each row's output is (within e^-20) the V row at its own position (or at
     position 0 for the reverse ramp): exercises the mask at every row, across
-    tiles, splits, pages and both kernels."""
+    tiles, splits, pages and both kernels.  The forward ramp's logits grow by
+    thousands of base-2 units from step to step, so weights taken against the
+    first step's max overflow: the paired tiles (tpb 2) must notice it and run
+    again with the running max."""
     spec = synth.build("ramp", "bf16", 32, 8, 128, 16, [300, 1, 2, 1], [1300, 2000, 513, 17], 5,
                        np.random.default_rng(5), 1.2)
     ht = synth.host_tensors(spec)
     _ramp(spec, ht, reverse)
     ref, _, kp, vp = oracle.store_then_attend(spec, ht, nthreads=8)
     db = H.dev_batch(spec, ht)
-    out, plan = H.gpu_forward(spec, db, split_min_keys=64)
+    out, plan = H.gpu_forward(spec, db, split_min_keys=64, tiles_per_block=tpb)
+    assert plan.info()["tiles_per_block"] == tpb
     got = H.to_f64(out)
     cu = spec.cu_q
     for i in range(spec.bs):
