@@ -201,7 +201,7 @@ __device__ __forceinline__ bool pair_group(const AttnArgs &a, const Item &it, co
   const int kx = swz(q32);
   const int vg = lane >> 4, vj = (lane & 15) >> 2, vq = lane & 3;
   const int vrow = 4 * half + vj;
-  const int vx = swz(vrow);
+  const int vx = swz(vrow), vxh = swz(vrow + 8);
   const int vc0 = 2 * (vg & 1) + (vq >> 1);
 
   f32x16 s[2];
@@ -283,7 +283,7 @@ __device__ __forceinline__ bool pair_group(const AttnArgs &a, const Item &it, co
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const v4i16 lo = tr_read(rp + 16 * ((vc0 + 4 * db) ^ vx));
-        const v4i16 hi = tr_read(rp + 8 * ROWB + 16 * ((vc0 + 4 * db) ^ vx ^ 1));
+        const v4i16 hi = tr_read(rp + 8 * ROWB + 16 * ((vc0 + 4 * db) ^ vxh));
         dst[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
@@ -466,6 +466,9 @@ __device__ __forceinline__ bool pair_group(const AttnArgs &a, const Item &it, co
     if (BIGPAGE) {
       uint32_t off[4];
       const char *sb = step_addr(ids, r + 2, pool, off);
+      // the ids of step r+3 go out now (a scalar load: the next matrix
+      // phase's first LDS wait would otherwise cover it too)
+      fetch_ids(ids, kbeg + (r + 3) * BN);
       if (own) {
         softmax(r, [&](int h) {
           // the scheduler keeps each load between the blocks of work around it
@@ -486,7 +489,7 @@ __device__ __forceinline__ bool pair_group(const AttnArgs &a, const Item &it, co
     // softmax is moved past the wait.)
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(ppair::vmcnt_imm(4));
-    fetch_ids(ids, kbeg + (r + 3) * BN);
+    if (!BIGPAGE) fetch_ids(ids, kbeg + (r + 3) * BN);
   };
 
   // ---- rounds 0..T, three at a time so every buffer is a fixed address; then
