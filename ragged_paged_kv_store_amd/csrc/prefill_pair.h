@@ -48,6 +48,10 @@ namespace ppair {
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 }  // namespace ppair
 
+// One group's tile of a pair (group GRP, its wavefronts lw = 0..3).  EXACT =
+// false: each row's softmax reference is its max over the first step; returns
+// true, having written nothing, when the workgroup must run its tiles again
+// with EXACT = true, the running max of every step (see prefill_pair).
 template <int PM, int GRP, bool EXACT>
 __device__ __forceinline__ bool pair_group(const AttnArgs &a, const Item &it, const int kbeg,
                                            const int kend_u, const int T, unsigned char *Kbuf,
