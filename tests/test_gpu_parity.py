@@ -183,9 +183,13 @@ def test_ramp_probe_pins_mask_boundary(reverse, tpb):
     assert H.max_err(out, ref) <= 2e-2
 
 
-def test_needles_at_page_split_and_prefix_boundaries():
+@pytest.mark.parametrize("tpb", [0, 2])
+def test_needles_at_page_split_and_prefix_boundaries(tpb):
     """One dominant key placed around page, 32/64-key step, split-chunk and
-    cascade-prefix boundaries: a row's output is that key's V iff it is visible."""
+    cascade-prefix boundaries: a row's output is that key's V iff it is visible.
+    The needle's logit exceeds the others by about 65 base-2 units, so with two
+    tiles per workgroup (tpb 2) a needle past a tile's first step takes the
+    second, running-max pass in cascade-level and split tiles too."""
     prefix = 640
     n_share = 6
     tails = [70, 100, 130, 64, 65, 200]
@@ -215,7 +219,7 @@ def test_needles_at_page_split_and_prefix_boundaries():
         # keep every other key's logit at 0: zero q components elsewhere already
         ref, _, kp, vp = oracle.store_then_attend(spec, ht, nthreads=8)
         db = H.dev_batch(spec, ht)
-        out, plan = H.gpu_forward(spec, db, split_min_keys=64)
+        out, plan = H.gpu_forward(spec, db, split_min_keys=64, tiles_per_block=tpb)
         assert plan.info()["cascade_members"] == n_share
         assert H.max_err(out, ref) <= 2e-2, p
 
