@@ -388,7 +388,11 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
     }
   } else {
     if (!rowv) return;
-    const int64_t pi = (int64_t)pbase + it.split;
+    // (the load of pbase is first read here: opaque until now, so no wait for
+    // it is placed in the prologue)
+    int32_t pb = pbase;
+    asm volatile("" : "+v"(pb));
+    const int64_t pi = (int64_t)pb + it.split;
     float *prow = a.o_part + (pi * a.Hq + qh) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
