@@ -154,16 +154,18 @@ def _ramp(spec, ht, reverse=False):
         ht.k[cu[i]:cu[i + 1]] = synth.f32_to_bf16_bits(-K if reverse else K)
 
 
+@pytest.mark.parametrize("n_new", [300, 270])
 @pytest.mark.parametrize("tpb", [1, 2])
 @pytest.mark.parametrize("reverse", [False, True])
-def test_ramp_probe_pins_mask_boundary(reverse, tpb):
+def test_ramp_probe_pins_mask_boundary(reverse, tpb, n_new):
     """Each row's output is (within e^-20) the V row at its own position (or at
     position 0 for the reverse ramp): exercises the mask at every row, across
     tiles, splits, pages and both kernels.  The forward ramp's logits grow by
     thousands of base-2 units from step to step, so weights taken against the
     first step's max overflow: the paired tiles (tpb 2) must notice it and run
-    again with the running max."""
-    spec = synth.build("ramp", "bf16", 32, 8, 128, 16, [300, 1, 2, 1], [1300, 2000, 513, 17], 5,
+    again with the running max.  With 270 new tokens the chunk has 9 tiles, so
+    one pair has a load-only partner group."""
+    spec = synth.build("ramp", "bf16", 32, 8, 128, 16, [n_new, 1, 2, 1], [1000 + n_new, 2000, 513, 17], 5,
                        np.random.default_rng(5), 1.2)
     ht = synth.host_tensors(spec)
     _ramp(spec, ht, reverse)
