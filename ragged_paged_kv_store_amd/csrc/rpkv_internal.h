@@ -47,9 +47,13 @@ constexpr int kPrefillSlots = 512;    // MI355X: 256 CUs x 2 resident prefill ti
 // deepest nesting of shared-prefix levels the planner keeps (the keys of deeper
 // levels are read by their members as part of the level above or their tails)
 constexpr int kMaxCascadeDepth = 16;
-// keys one split-KV wavefront streams while a co-resident MFMA tile runs one
-// 64-key step (measured rates: ~2.5 us per tile step, ~20 keys/us per chunk)
-constexpr int kConcurrentKeysPerStep = 24;
+// In a mixed launch a split-KV chunk is sized to the tiles' critical path:
+// this many keys per 64-key tile step of it.  (A chunk streams ~20 keys/us
+// beside tiles that take ~2 us per step, so 8 ends the chunks at about a third
+// of the critical path, freeing their slots for the last tiles; measured
+// against 4-32: C2's launch -6.7% and radix -9.3% against 24, with the merge
+// included -3.4% and -6.3%; C4 and C5 unchanged; below 8 the merge grows.)
+constexpr int kConcurrentKeysPerStep = 8;
 
 // One level of the shared-prefix tree.  Its members attend the keys between the
 // parent level's prefix (0 at the top) and `prefix` once, stacked together in
