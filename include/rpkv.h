@@ -319,10 +319,15 @@ rpkv_status rpkv_plan_summary(const rpkv_plan *plan, char *buf, size_t size);
 
 /* Host copy of the last plan's work items for inspection: kind 0 = prefill
  * tiles, 1 = decode chunks.  Each item is 8 int32: request, KV head, first
- * token (or cascade token-list offset), token count, position of the first
- * token (-1 for a cascade prefix tile), key begin, key end, split index (-1 =
- * final output).  Padding items (token count 0) are included.  Writes
- * min(capacity, count) items; *count receives the total. */
+ * token (or cascade token-list offset), token count (bits 0..15) with a row
+ * offset (bits 16..23), position of the first token (-1 for a cascade prefix
+ * tile), key begin, key end, split index (-1 = final output).  An item's rows
+ * are its tokens' (token, head) rows in token-major order (row j: token
+ * first + j / G, head KV head * G + j % G), starting at the row offset and
+ * holding at most 128 rows (a bf16 tile) -- the offset is nonzero only where a
+ * request's rows are cut every 128 rows for G not dividing 128.  Padding items
+ * (token count 0) are included.  Writes min(capacity, count) items; *count
+ * receives the total. */
 rpkv_status rpkv_plan_get_items(const rpkv_plan *plan, int32_t kind, int32_t *items_host,
                                 int32_t capacity, int32_t *count);
 

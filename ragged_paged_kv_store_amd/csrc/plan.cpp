@@ -646,17 +646,13 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
     pre.reserve(nt + nt / 2);
     pre_key.reserve(nt + nt / 2);
   }
+  // the steps of the token-aligned tiles set the fair share of the key splits
   int64_t total_steps = 0;
   for (int32_t i = 0; i < batch; ++i) {
     const int32_t n = n_of(i);
     if (n == 0 || is_decode(i)) continue;
-    for (int32_t h = 0; h < s.Hkv; ++h)
-      for (int32_t r0 = 0; r0 < n; r0 += tpt) {
-        const int32_t r1 = std::min(n, r0 + tpt);
-        tiles.push_back(Item{i, h, cu[i] + r0, r1 - r0, L[i] - n + r0, 0, L[i] - n + r1, -1});
-        tile_key.push_back((int64_t)i * s.Hkv + h);
-        total_steps += cdiv(L[i] - n + r1, kPrefillKeys);
-      }
+    for (int32_t r0 = 0; r0 < n; r0 += tpt)
+      total_steps += cdiv(L[i] - n + std::min(n, r0 + tpt), kPrefillKeys) * s.Hkv;
   }
   // A tile much longer than the fair share of steps per concurrent tile slot
   // would set the launch's critical path: cut its key range into pieces of whole
@@ -665,6 +661,35 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
   // at the same keys, from the longer one's length, so a workgroup running two
   // of them can share one K/V stream.
   const int64_t fair = std::max<int64_t>(8, cdiv(total_steps, kPrefillSlots));
+  auto never_split = [&](int32_t i) { return cdiv(L[i], kPrefillKeys) <= fair + fair / 2; };
+  // Tiles hold 128 / G whole tokens, except where G does not divide 128 and no
+  // tile of the request is split: there the tiles cut the request's (token,
+  // head) rows every 128 rows, so a token's heads may straddle two tiles (a
+  // split tile's partials are counted per token, hence whole tokens there).
+  // For G = 7 a 512-token chunk then takes 28 tiles of 128 rows instead of 29
+  // of 18 tokens (the last holding 8).
+  for (int32_t i = 0; i < batch; ++i) {
+    const int32_t n = n_of(i);
+    if (n == 0 || is_decode(i)) continue;
+    const bool rowcut = !f32 && kPrefillRows % G != 0 && never_split(i);
+    for (int32_t h = 0; h < s.Hkv; ++h) {
+      if (rowcut) {
+        const int64_t R = (int64_t)n * G;
+        for (int64_t k = 0; k < R; k += kPrefillRows) {
+          const int32_t ft = (int32_t)(k / G), lt = (int32_t)((std::min<int64_t>(R, k + kPrefillRows) - 1) / G);
+          tiles.push_back(Item{i, h, cu[i] + ft, pack_ntok(lt - ft + 1, (int32_t)(k - (int64_t)ft * G)),
+                               L[i] - n + ft, 0, L[i] - n + lt + 1, -1});
+          tile_key.push_back((int64_t)i * s.Hkv + h);
+        }
+        continue;
+      }
+      for (int32_t r0 = 0; r0 < n; r0 += tpt) {
+        const int32_t r1 = std::min(n, r0 + tpt);
+        tiles.push_back(Item{i, h, cu[i] + r0, r1 - r0, L[i] - n + r0, 0, L[i] - n + r1, -1});
+        tile_key.push_back((int64_t)i * s.Hkv + h);
+      }
+    }
+  }
   for (size_t k = 0; k < tiles.size();) {
     const bool sib = k + 1 < tiles.size() && tile_key[k + 1] == tile_key[k];
     const size_t kn = sib ? k + 2 : k + 1;
@@ -681,7 +706,7 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
         pre_key.push_back(tile_key[u]);
         continue;
       }
-      for (int32_t tk = t.tok0; tk < t.tok0 + t.ntok; ++tk) nsplit[tk] = (int32_t)tparts;
+      for (int32_t tk = t.tok0; tk < t.tok0 + item_ntok(t); ++tk) nsplit[tk] = (int32_t)tparts;
       for (int64_t pc = 0; pc < tparts; ++pc) {
         Item piece = t;
         piece.kbeg = (int32_t)(pc * per);
@@ -755,6 +780,16 @@ rpkv_status plan_batch_host(const Shape &s, int32_t batch, const int32_t *cu, co
     }
     const int64_t est_steps = std::max(longest, cdiv(steps_all, kPrefillSlots));
     chunk64 = std::max(chunk64, round_up(est_steps * kConcurrentKeysPerStep, kDecodeKeys));
+    // When no tile writes partials and every decode's range is within half a
+    // chunk more than that, one chunk per request: the merge launch would
+    // otherwise run for a handful of tokens.
+    bool tile_partials = nlev > 0;
+    for (const Item &it : pre) tile_partials |= it.split >= 0;
+    int64_t dmax = 0;
+    for (int32_t i = 0; i < batch; ++i)
+      if (is_decode(i)) dmax = std::max<int64_t>(dmax, L[i] - own_from(i));
+    if (!tile_partials && dmax > chunk64 && 2 * dmax <= 3 * chunk64)
+      chunk64 = round_up(dmax, kDecodeKeys);
   }
   const int32_t chunk = (int32_t)std::min<int64_t>(chunk64, 1 << 30);
   p.decode_chunk = chunk;

@@ -62,14 +62,17 @@ __device__ __forceinline__ bool pair_group(const AttnArgs &a, const Item &it, co
   const int lane = threadIdx.x & 63;
   const int q32 = lane & 31, half = lane >> 5;
   const int G = a.G;
-  const int rows = it.ntok * G;
+  const int ntok = item_ntok(it);
+  const int rows = item_rows(it, G, kPrefillRows);
   const bool casc = it.pos0 < 0;
 
+  // mr: this lane's row in the item's token run
   const int m = lw * 32 + q32;
   const bool rowv = m < rows;
+  const int mr = m + item_row0(it);
   // (a group without a tile reads no token data)
-  const int tl = rowv ? m / G : (own ? it.ntok - 1 : 0);
-  const int gg = rowv ? m % G : 0;
+  const int tl = rowv ? mr / G : (own ? ntok - 1 : 0);
+  const int gg = rowv ? mr % G : 0;
   const int tok = !own ? 0 : casc ? a.toklist[it.tok0 + tl] : it.tok0 + tl;
   const int qh = it.kvh * G + gg;
   const int apos = casc ? INT32_MAX : it.pos0 + tl;

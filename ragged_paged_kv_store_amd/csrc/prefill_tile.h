@@ -2,7 +2,9 @@
 //
 // One workgroup (4 wavefronts) owns one tile of up to 128 query rows of one KV
 // head: 128/G tokens x the G query heads that share the KV head (token-major),
-// so every K/V byte staged in LDS feeds G heads.  Each wavefront owns 32 rows.
+// so every K/V byte staged in LDS feeds G heads.  (Where G does not divide 128
+// a tile may instead hold 128 consecutive (token, head) rows starting inside a
+// token: the item's row offset.)  Each wavefront owns 32 rows.
 //
 // Per 64-key step:
 //  * K and V rows of the next step are gathered through the page table straight
@@ -83,14 +85,16 @@ __device__ __forceinline__ void prefill_tile(const AttnArgs &a, int tile) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int q32 = lane & 31, half = lane >> 5;
   const int G = a.G;
-  const int rows = it.ntok * G;
+  const int ntok = item_ntok(it);
+  const int rows = item_rows(it, G, kPrefillRows);
   const bool casc = it.pos0 < 0;
 
-  // ---- this lane's query row (column of S^T)
+  // ---- this lane's query row (column of S^T); mr: its row in the token run
   const int m = wave * 32 + q32;
   const bool rowv = m < rows;
-  const int tl = rowv ? m / G : it.ntok - 1;
-  const int gg = rowv ? m % G : 0;
+  const int mr = m + item_row0(it);
+  const int tl = rowv ? mr / G : ntok - 1;
+  const int gg = rowv ? mr % G : 0;
   const int tok = casc ? a.toklist[it.tok0 + tl] : it.tok0 + tl;
   const int qh = it.kvh * G + gg;
   const int apos = casc ? INT32_MAX : it.pos0 + tl;

@@ -19,7 +19,9 @@ struct Item {
   int32_t req;   // request index: its page-table row is read
   int32_t kvh;   // KV head
   int32_t tok0;  // first packed token, or offset into the cascade token list
-  int32_t ntok;  // tokens in the tile; 0 = padding item (skipped)
+  int32_t ntok;  // low 16 bits: tokens the tile touches (0 = padding item,
+                 // skipped); bits 16..23: rows of the first token that precede
+                 // the tile (see item_rows)
   int32_t pos0;  // absolute position of tok0's query; -1 marks a cascade prefix
                  // tile (tokens from the list, every key in range visible)
   int32_t kbeg;  // keys [kbeg, kend) of the request are attended
@@ -28,6 +30,25 @@ struct Item {
                  // `split` of each token (partial index tok_pbase[t] + split)
 };
 static_assert(sizeof(Item) == 32, "Item is 8 int32");
+
+// The rows of an item are a run of the (token, head-in-group) rows of its
+// tokens, token-major: run row j is token tok0 + j / G, query head kvh*G + j % G.
+// A tile starts `item_row0` rows into the run (0 unless the tile was cut at a
+// multiple of 128 rows inside a token, for G not dividing 128) and holds the
+// rest of the run up to `cap` rows.
+#if defined(__HIP__)
+#define RPKV_HD __attribute__((host, device, always_inline)) inline
+#else
+#define RPKV_HD inline
+#endif
+RPKV_HD int32_t item_ntok(const Item &it) { return it.ntok & 0xffff; }
+RPKV_HD int32_t item_row0(const Item &it) { return (it.ntok >> 16) & 0xff; }
+RPKV_HD int32_t item_rows(const Item &it, int32_t G, int32_t cap) {
+  const int32_t r = item_ntok(it) * G - item_row0(it);
+  return r < cap ? r : cap;
+}
+RPKV_HD int32_t pack_ntok(int32_t ntok, int32_t row0) { return ntok | (row0 << 16); }
+#undef RPKV_HD
 
 constexpr int kPrefillRows = 128;     // bf16 MFMA tile: 4 waves x 32 rows
 constexpr int kPrefillKeys = 64;      // keys per LDS tile

@@ -70,11 +70,28 @@ bool check_partition(const Batch &b, const rpkv::Shape &s, const rpkv::HostPlan 
     if (it.ntok == 0) return true;
     CHECK(0 <= it.kbeg && it.kbeg < it.kend, "empty or negative key range");
     CHECK(it.kvh >= 0 && it.kvh < s.Hkv, "bad KV head");
-    const int32_t rows = it.ntok * G;
-    if (decode) CHECK(rows <= rpkv::kDecodeRows, "decode item of %d rows", rows);
-    else CHECK(rows <= (s.dtype == RPKV_F32 ? rpkv::kF32Rows : rpkv::kPrefillRows) || it.ntok == 1,
-               "tile of %d rows", rows);
-    for (int32_t r = 0; r < it.ntok; ++r) {
+    // a tile's rows: a run of its tokens' (token, head) rows from row0 on
+    const int32_t ntok = rpkv::item_ntok(it), row0 = rpkv::item_row0(it);
+    const int32_t cap = decode ? rpkv::kDecodeRows
+                               : (s.dtype == RPKV_F32 ? rpkv::kF32Rows : rpkv::kPrefillRows);
+    CHECK(ntok > 0 && row0 >= 0 && row0 < G, "token count %d, row offset %d", ntok, row0);
+    if (decode) CHECK(ntok * G <= cap && row0 == 0, "decode item of %d rows", ntok * G);
+    if (row0 > 0 || ntok * G > cap) {
+      // cut every 128 rows inside a token: unsplit bf16 tiles, G not dividing 128
+      CHECK(!decode && s.dtype == RPKV_BF16 && rpkv::kPrefillRows % G != 0 && it.split < 0 &&
+                it.pos0 >= 0,
+            "row-cut item that may not be cut");
+      const int64_t first = (int64_t)(it.tok0 - b.cu[it.req]) * G + row0;
+      const int64_t last = first + rpkv::item_rows(it, G, cap);
+      const int64_t R = (int64_t)(b.cu[it.req + 1] - b.cu[it.req]) * G;
+      CHECK(first % cap == 0 && (last % cap == 0 || last == R), "row cut at %lld..%lld",
+            (long long)first, (long long)last);
+      CHECK((ntok - 1) * G < row0 + cap, "tile of %d tokens from row %d", ntok, row0);
+    } else {
+      CHECK(ntok * G <= cap || ntok == 1, "tile of %d rows", ntok * G);
+    }
+    const int32_t nrows = decode ? ntok * G : rpkv::item_rows(it, G, ntok == 1 ? ntok * G : cap);
+    for (int32_t r = 0; r < ntok; ++r) {
       int32_t t, hi;
       if (it.pos0 < 0) {
         CHECK(it.tok0 + r < (int32_t)hp.toklist.size(), "token list index");
@@ -92,8 +109,11 @@ bool check_partition(const Batch &b, const rpkv::Shape &s, const rpkv::HostPlan 
         CHECK(it.kend <= b.L[it.req], "key range past L");
         hi = std::min(it.kend, a_of[t] + 1);
       }
-      for (int32_t g = 0; g < G; ++g)
+      for (int32_t g = 0; g < G; ++g) {
+        const int32_t j = r * G + g - row0;  // row of the tile
+        if (j < 0 || j >= nrows) continue;
         seg[(size_t)t * s.Hq + it.kvh * G + g].emplace_back(it.kbeg, hi, it.split);
+      }
     }
     return true;
   };

@@ -169,14 +169,28 @@ def check_coverage(rp, plan, spec):
     cover = {}
     for kind in (0, 1):
         for it in plan.items(kind):
-            req, kvh, tok0, ntok, pos0, kbeg, kend, split = [int(x) for x in it]
+            req, kvh, tok0, nfield, pos0, kbeg, kend, split = [int(x) for x in it]
+            # token count, and the rows of the first token before the tile
+            ntok, row0 = nfield & 0xFFFF, (nfield >> 16) & 0xFF
             if ntok == 0:
                 continue
             assert 0 <= kbeg < kend
-            if kind == 1:
-                assert ntok * G <= 16
+            cap = 16 if kind == 1 or spec.dtype != "bf16" else 128
+            if row0 or ntok * G > cap:
+                # rows cut every 128 inside a token: only for unsplit bf16 tiles
+                # with G not dividing 128, every cut at a multiple of 128 rows
+                assert kind == 0 and spec.dtype == "bf16" and 128 % G and split == -1 and pos0 >= 0
+                assert 0 <= row0 < G and (tok0 - int(cu[req])) * G + row0 == \
+                    ((tok0 - int(cu[req])) * G + row0) // 128 * 128
+                last_row = (tok0 - int(cu[req])) * G + row0 + min(cap, ntok * G - row0)
+                assert last_row % 128 == 0 or last_row == int(spec.n[req]) * G
+                assert (ntok - 1) * G < row0 + cap
             else:
-                assert ntok * G <= (128 if spec.dtype == "bf16" else 16) or ntok == 1
+                assert ntok * G <= cap or ntok == 1
+            rows = min(cap, ntok * G - row0) if kind == 0 else ntok * G
+            heads_of = {}
+            for j in range(row0, row0 + rows):
+                heads_of.setdefault(j // G, []).append(j % G)
             for r in range(ntok):
                 if pos0 < 0:
                     t = int(tl[tok0 + r])
@@ -196,7 +210,7 @@ def check_coverage(rp, plan, spec):
                         "cascade tile reads pages a row's request does not share"
                     hi = kend
                 assert kend <= int(spec.L[i]) or pos0 < 0
-                for g in range(G):
+                for g in heads_of[r]:
                     h = kvh * G + g
                     cover.setdefault((t, h), []).append((kbeg, hi, split))
     for t in range(spec.T):
