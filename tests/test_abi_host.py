@@ -334,3 +334,21 @@ def test_tiles_per_block_choice_and_pair_layout(rp):
                         tiles_per_block=3)
     assert not ok
 
+
+
+def test_row_cut_tiles_covered_exactly_once(rp):
+    """The row-cut cases of the GPU test plan tiles that start inside a token
+    beside key-split whole-token tiles, in both tile arrangements, and cover
+    every visible (token, head, key) exactly once."""
+    from tests.test_gpu_row_cut import CASES
+    for name, Hq, Hkv, n, L in CASES:
+        spec = synth.build(name, "bf16", Hq, Hkv, 128, 16, n, L, 31, np.random.default_rng(0), 1.25)
+        for tpb in (1, 2):
+            p = make_plan(rp, spec, tiles_per_block=tpb)
+            p.plan_host(spec.cu_q, spec.L, spec.page_table.shape[1], spec.page_table)
+            items = p.items(0)
+            assert ((items[:, 3] >> 16) > 0).any(), name
+            assert (items[:, 7] >= 0).any(), name
+            check_coverage(rp, p, spec)
+            if tpb == 2:
+                check_sibling_pairs(p)
