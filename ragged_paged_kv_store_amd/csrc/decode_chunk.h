@@ -18,8 +18,11 @@
 //  * loads V rows (16 B per lane: 8 channels of one key), transposes them in
 //    registers into A operands of O^T = V^T P^T, and accumulates with 8 MFMAs
 //    (output row m of virtual block c is channel 8m + c).
-// Loads of step t+1 and page-table reads of step t+2 are issued before step t
-// is computed (two register sets, no copies).
+// K and V are read with nontemporal loads: each byte is read once (a read-only
+// probe streams 7.0 TB/s so, against 6.3-6.8 with plain loads; a batch of 256
+// decodes over 1k-8k keys runs 6% faster).  Loads of step t+1 and page-table
+// reads of step t+2 are issued before step t is computed (two register sets,
+// no copies).
 // The item writes its rows' final output, or a partial result (normalised O in
 // fp32 plus the base-2 log-sum-exp) for the merge kernel.
 #pragma once
@@ -96,10 +99,10 @@ __device__ __forceinline__ void load(Regs &r, const SlotsSmall &s, const char *k
 #pragma unroll
     for (int st = 0; st < 4; ++st)
       r.k[sb][st] =
-          *(const u32x4 *)(kpool + row_bytes_off(s.k[sb], hkv, kvh) + (st * 32 + grp * 8) * 2);
+          __builtin_nontemporal_load((const u32x4 *)(kpool + row_bytes_off(s.k[sb], hkv, kvh) + (st * 32 + grp * 8) * 2));
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    r.v[e] = *(const u32x4 *)(vpool + row_bytes_off(s.v[e], hkv, kvh) + col * 16);
+    r.v[e] = __builtin_nontemporal_load((const u32x4 *)(vpool + row_bytes_off(s.v[e], hkv, kvh) + col * 16));
 }
 
 __device__ __forceinline__ void load(Regs &r, const SlotsBig &s, const char *kpool,
@@ -113,10 +116,10 @@ __device__ __forceinline__ void load(Regs &r, const SlotsBig &s, const char *kpo
     const int32_t s0 = (s.pg[sb] << log2P) + ((kb + 16 * sb) & pmask);
     const char *kbase = kpool + row_bytes_off(s0, hkv, kvh) + (int64_t)col * rowb;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) r.k[sb][st] = *(const u32x4 *)(kbase + (st * 32 + grp * 8) * 2);
+    for (int st = 0; st < 4; ++st) r.k[sb][st] = __builtin_nontemporal_load((const u32x4 *)(kbase + (st * 32 + grp * 8) * 2));
     const char *vbase = vpool + row_bytes_off(s0, hkv, kvh) + (int64_t)(4 * grp) * rowb + col * 16;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r.v[4 * sb + e] = *(const u32x4 *)(vbase + e * rowb);
+    for (int e = 0; e < 4; ++e) r.v[4 * sb + e] = __builtin_nontemporal_load((const u32x4 *)(vbase + e * rowb));
   }
 }
 
