@@ -5,7 +5,9 @@ namespace rpkv {
 
 template <class Slots>
 __global__ __launch_bounds__(256, 2) void attn_decode_bf16_kernel(AttnArgs a) {
-  decode_chunk<Slots>(a, blockIdx.x);
+  // K rows staged in LDS, two steps per wavefront (64 KiB for the block)
+  __shared__ __attribute__((aligned(1024))) unsigned char stage[kDecodeWavesPerBlock * dchunk::kStageBytes];
+  decode_chunk<Slots>(a, blockIdx.x, stage);
 }
 
 int launch_decode_bf16(const AttnArgs &a, void *stream) {
@@ -40,6 +42,7 @@ __global__ __launch_bounds__(256, 2) void attn_graph_decode_bf16_kernel(AttnArgs
                                                                         int32_t q_len, int32_t chunk,
                                                                         int32_t maxc, int32_t max_seq,
                                                                         int32_t batch) {
+  __shared__ __attribute__((aligned(1024))) unsigned char stage[kDecodeWavesPerBlock * dchunk::kStageBytes];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ii = blockIdx.x * kDecodeWavesPerBlock + wave;
   if (ii >= batch * maxc * a.Hkv) return;
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(256, 2) void attn_graph_decode_bf16_kernel(AttnArgs
   const int nch = (L + chunk - 1) / chunk;  // <= maxc
   if (c >= nch) return;
   const Item it{i, h, i * q_len, q_len, L - q_len, c * chunk, min(L, (c + 1) * chunk), nch > 1 ? c : -1};
-  decode_item<Slots>(a, it);
+  decode_item<Slots, true>(a, it, stage + wave * dchunk::kStageBytes);
 }
 
 int launch_graph_decode_bf16(const AttnArgs &a, const int32_t *seq_lens, int32_t q_len,
