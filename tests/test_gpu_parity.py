@@ -92,6 +92,12 @@ EDGE = [
     ("long_prefill_many_tiles", "bf16", 16, 2, 16, [700], [1500]),
     ("f32_prefill_tiles", "f32", 8, 2, 4, [40, 1, 7], [40, 99, 30]),
     ("f32_page1_mha", "f32", 4, 4, 1, [9, 1], [20, 64]),
+    # decode-only batches run the split-KV kernel on its own (K staged in LDS),
+    # with per-key page lookups below 16 keys per page
+    ("decode_only_page1", "bf16", 16, 4, 1, [1, 2, 1], [37, 300, 1000]),
+    ("decode_only_page4", "bf16", 32, 8, 4, [1, 1, 3, 1], [5, 333, 777, 2050]),
+    ("decode_only_page8", "bf16", 28, 4, 8, [2, 1], [2, 1500]),
+    ("decode_only_page64", "bf16", 32, 2, 64, [1, 1, 1], [65, 129, 3000]),
 ]
 
 
