@@ -4,8 +4,9 @@ The workloads at their stated sizes, in the launch configuration the benchmark
 times (the planner's own choices), compared element by element with the fp64
 oracle on many more rows than the sampled test: every row of the
 Llama-3-8B-shaped mixed batch (the 2000-token prefill's every tile and key
-split), every row of one 512-token chunk over 4096 cached tokens plus every
-decode of the chunked-prefill batch, and in the shared-prefix batch every
+split), every one of the 256 decodes of the decode-heavy batch, every row of one
+512-token chunk over 4096 cached tokens plus every decode of the chunked-prefill
+batch, and in the shared-prefix batch every
 cascade member plus the first and last row of every 16-token tile of one
 4096-token chunk over 28672 cached tokens.  The oracle runs on the sub-problem
 of exactly the pages those requests reference, taken from the device before the
@@ -71,6 +72,15 @@ def test_llama3_8b_mixed_every_row():
     _, plan = run_dense(2, list(range(spec.bs)), every_row)
     # the long prefill's longest tiles are split by keys and merged
     assert plan.info()["num_merge_tokens"] > 6
+
+
+def test_decode_heavy_every_decode():
+    # the split-KV kernel in a launch of its own (K staged through LDS), every
+    # one of the 256 decodes and its chunks' merge
+    spec = synth.full_config(3)
+    _, plan = run_dense(3, list(range(spec.bs)), every_row)
+    info = plan.info()
+    assert info["num_prefill_items"] == 0 and info["num_merge_tokens"] > 200
 
 
 def test_chunked_prefill_one_chunk_and_every_decode():
