@@ -352,3 +352,25 @@ def test_row_cut_tiles_covered_exactly_once(rp):
             check_coverage(rp, p, spec)
             if tpb == 2:
                 check_sibling_pairs(p)
+
+
+def test_mixed_launch_stretches_chunks_rather_than_merge_a_few_decodes(rp):
+    """In a launch with MFMA tiles and no tile partials, decodes up to half a
+    chunk longer than the split-KV chunk run as one chunk each (no merge launch
+    for a handful of tokens); longer ones are still split."""
+    def info(L_dec):
+        n = [512] * 4 + [1] * len(L_dec)
+        L = [4608] * 4 + list(L_dec)
+        spec = synth.build("stretch", "bf16", 28, 4, 128, 16, n, L, 3, np.random.default_rng(0), 1.25)
+        p = make_plan(rp, spec)
+        p.plan_host(spec.cu_q, spec.L, spec.page_table.shape[1], spec.page_table)
+        check_coverage(rp, p, spec)
+        return p.info()
+    base = info([300, 500])
+    chunk = base["decode_chunk"]
+    assert base["num_partials"] == 0 and base["num_prefill_items"] > 0
+    for L in (chunk + 40, chunk * 3 // 2 - 32):
+        i = info([300, L])
+        assert i["num_partials"] == 0 and i["decode_chunk"] >= L, (L, i)
+    i = info([300, chunk * 3 // 2 + 64])
+    assert i["num_partials"] == 2 and i["decode_chunk"] == chunk
