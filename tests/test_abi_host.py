@@ -240,6 +240,20 @@ def test_small_configs_covered_exactly_once(rp, cid):
         assert p.info()["cascade_members"] == spec.groups[0][1]
 
 
+@pytest.mark.parametrize("tpb", [0, 1, 2])
+@pytest.mark.parametrize("Hq,Hkv,n,L", [
+    (64, 1, [5, 1, 2], [300, 700, 41]),      # 2 tokens x 64 heads per tile
+    (128, 1, [3, 1, 1], [600, 257, 1]),      # 1 token x 128 heads per tile
+    (128, 2, [1, 1, 1], [100, 2000, 5000]),  # decodes of 64 rows run as tiles
+])
+def test_largest_groups_covered_exactly_once(rp, Hq, Hkv, n, L, tpb):
+    spec = synth.build("bigG", "bf16", Hq, Hkv, 128, 16, n, L, 7, np.random.default_rng(Hq + Hkv), 1.3)
+    p = make_plan(rp, spec, tiles_per_block=tpb)
+    p.plan_host(spec.cu_q, spec.L, spec.page_table.shape[1], spec.page_table)
+    check_coverage(rp, p, spec)
+    assert len(p.items(1)) == 0, "n * G > 16: no split-KV items"
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_random_batches_covered_exactly_once(rp, seed):
     rng = np.random.default_rng(seed)

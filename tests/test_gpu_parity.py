@@ -90,6 +90,11 @@ EDGE = [
     ("spec_decode_n2_g8", "bf16", 64, 8, 16, [2, 2, 3], [50, 513, 100]),
     ("threshold_n4_g4", "bf16", 32, 8, 16, [4, 5], [200, 200]),
     ("long_prefill_many_tiles", "bf16", 16, 2, 16, [700], [1500]),
+    # the largest group sizes the bf16 kernels take: tiles of 2 tokens x 64
+    # heads and of 1 token x 128 heads; decodes then run as tiles too
+    ("g64_two_tokens_per_tile", "bf16", 64, 1, 16, [5, 1, 2], [300, 700, 41]),
+    ("g128_one_token_per_tile", "bf16", 128, 1, 16, [3, 1, 1], [600, 257, 1]),
+    ("g64_decodes_only", "bf16", 128, 2, 16, [1, 1, 1], [100, 2000, 5000]),
     ("f32_prefill_tiles", "f32", 8, 2, 4, [40, 1, 7], [40, 99, 30]),
     ("f32_page1_mha", "f32", 4, 4, 1, [9, 1], [20, 64]),
     # decode-only batches run the split-KV kernel on its own (K staged in LDS),
