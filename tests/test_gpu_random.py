@@ -66,3 +66,41 @@ def test_random_batch_matches_oracle(seed):
     print(f"{spec.name}: G={spec.G} Hkv={spec.Hkv} P={spec.P} {spec.dtype} D={spec.D} "
           f"n={spec.n.tolist()} err {err:.2e} info {plan.info()}")
     assert err <= H.TOL[spec.dtype]
+
+
+def random_decode_spec(seed):
+    """A decode-only bf16 batch (every request has n * G <= 16 new rows), so the
+    split-KV kernel runs in a launch of its own with K staged through LDS."""
+    rng = np.random.default_rng(5000 + seed)
+    G = int(rng.choice([1, 2, 4, 7, 8, 16]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    P = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128]))
+    bs = int(rng.integers(1, 40))
+    nmax = max(1, 16 // G)
+    n, L = [], []
+    for _ in range(bs):
+        x = int(rng.integers(1, min(nmax, 3) + 1))
+        n.append(x)
+        L.append(x + int(rng.integers(0, int(rng.choice([40, 700, 6000])))))
+    spec = synth.build(f"random_decode{seed}", "bf16", G * Hkv, Hkv, 128, P, n, L, seed,
+                       np.random.default_rng(seed), 1.2)
+    kw = dict(split_min_keys=int(rng.choice([0, 32, 64, 256])),
+              split_target=int(rng.choice([0, 64, 512])))
+    return spec, kw
+
+
+@pytest.mark.parametrize("seed", range(96))
+def test_random_decode_batch_matches_oracle(seed):
+    spec, kw = random_decode_spec(seed)
+    ht = synth.host_tensors(spec)
+    ref, _, kp_ref, vp_ref = oracle.store_then_attend(spec, ht, nthreads=8)
+    db = H.dev_batch(spec, ht)
+    out, plan = H.gpu_forward(spec, db, groups=[], **kw)
+    info = plan.info()
+    assert info["num_prefill_items"] == 0 and info["num_decode_items"] > 0
+    assert np.array_equal(H.to_host_bits(spec, db.kpool), kp_ref), "K pool differs after store"
+    assert np.array_equal(H.to_host_bits(spec, db.vpool), vp_ref), "V pool differs after store"
+    err = H.max_err(out, ref)
+    print(f"{spec.name}: G={spec.G} Hkv={spec.Hkv} P={spec.P} n={spec.n.tolist()} "
+          f"L={spec.L.tolist()} err {err:.2e} chunk {info['decode_chunk']}")
+    assert err <= H.TOL["bf16"]
