@@ -76,6 +76,24 @@ def test_graph_decode_matches_oracle(case):
     assert err <= H.TOL["bf16"], f"{name}: max abs err {err:.3e}"
 
 
+def random_graph_case(seed):
+    rng = np.random.default_rng(7000 + seed)
+    G = int(rng.choice([1, 2, 4, 7, 8, 16]))
+    q_len = int(rng.integers(1, min(16 // G, 3) + 1))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    P = int(rng.choice([1, 4, 16, 64]))
+    bs = int(rng.integers(1, 41))
+    max_seq = int(rng.integers(q_len, 8001))
+    return (f"random{seed}", G * Hkv, Hkv, P, q_len, bs, max_seq)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_graph_decode_random_shapes(seed):
+    """Seeded uniform batches of random GQA ratio, KV heads, page size, q_len,
+    batch and max_seq_len, eager calls against the oracle."""
+    test_graph_decode_matches_oracle(random_graph_case(seed))
+
+
 def test_graph_decode_equals_planned_path():
     spec = uniform_batch("eq", 32, 8, 16, 1, 40, 5000, np.random.default_rng(5))
     ht = synth.host_tensors(spec)
