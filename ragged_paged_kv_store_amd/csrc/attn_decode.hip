@@ -3,24 +3,31 @@
 
 namespace rpkv {
 
+// The planned split-KV launch runs two wavefronts (two chunks) per workgroup,
+// 32 KiB of LDS, up to four workgroups per CU: a slot is handed to the next
+// workgroup as soon as its two chunks end.  (Measured against four per
+// workgroup: C3's launch 759 -> 723 us, 1.6-5.6% faster on other decode-only
+// batches; one per workgroup was slower than both.)
+constexpr int kPlannedDecodeWaves = 2;
+
 template <class Slots>
-__global__ __launch_bounds__(256, 2) void attn_decode_bf16_kernel(AttnArgs a) {
-  // K rows staged in LDS, two steps per wavefront (64 KiB for the block)
-  __shared__ __attribute__((aligned(1024))) unsigned char stage[kDecodeWavesPerBlock * dchunk::kStageBytes];
-  decode_chunk<Slots>(a, blockIdx.x, stage);
+__global__ __launch_bounds__(64 * kPlannedDecodeWaves, 8 / kPlannedDecodeWaves) void attn_decode_bf16_kernel(AttnArgs a) {
+  // K rows staged in LDS, two steps per wavefront
+  __shared__ __attribute__((aligned(1024))) unsigned char stage[kPlannedDecodeWaves * dchunk::kStageBytes];
+  decode_chunk<Slots, kPlannedDecodeWaves>(a, blockIdx.x, stage);
 }
 
 int launch_decode_bf16(const AttnArgs &a, void *stream) {
   if (a.n_items <= 0) return 0;
-  const int blocks = (a.n_items + kDecodeWavesPerBlock - 1) / kDecodeWavesPerBlock;
+  const int blocks = (a.n_items + kPlannedDecodeWaves - 1) / kPlannedDecodeWaves;
   // pages of >= 16 keys: 16-key blocks of a step lie in one page (chunks start
   // on multiples of 32 keys or at a cascade prefix length, a multiple of the page)
   if (a.log2P >= 4)
     hipLaunchKernelGGL(attn_decode_bf16_kernel<dchunk::SlotsBig>, dim3(blocks),
-                       dim3(64 * kDecodeWavesPerBlock), 0, (hipStream_t)stream, a);
+                       dim3(64 * kPlannedDecodeWaves), 0, (hipStream_t)stream, a);
   else
     hipLaunchKernelGGL(attn_decode_bf16_kernel<dchunk::SlotsSmall>, dim3(blocks),
-                       dim3(64 * kDecodeWavesPerBlock), 0, (hipStream_t)stream, a);
+                       dim3(64 * kPlannedDecodeWaves), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
