@@ -92,7 +92,7 @@ typedef struct rpkv_shape {
                                 n*Hq/Hkv <= this (default 16, at most 16)      */
   int32_t split_target;      /* tuning: target number of decode work items per
                                 launch when choosing split-KV chunks (default
-                                4096)                                           */
+                                3072)                                           */
   int32_t split_min_keys;    /* tuning: smallest split-KV chunk in keys
                                 (default 64; rounded up to 32)                  */
   int32_t prefix_detect_keys;/* cascade: when > 0, a batch planned with a host

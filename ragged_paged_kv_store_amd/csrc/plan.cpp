@@ -105,7 +105,7 @@ rpkv_status check_shape(const rpkv_shape *s, Shape *o, std::string *msg) {
   o->num_pages = s->num_pages;
   o->max_tokens = s->max_tokens;
   o->decode_max_rows = s->decode_max_rows ? s->decode_max_rows : kDecodeRows;
-  o->split_target = s->split_target ? s->split_target : 4096;
+  o->split_target = s->split_target ? s->split_target : 3072;
   o->split_min_keys = (int32_t)round_up(s->split_min_keys ? s->split_min_keys : 64, kDecodeKeys);
   o->prefix_detect_keys = s->prefix_detect_keys;
   o->tiles_per_block = s->tiles_per_block;

@@ -76,11 +76,11 @@ def test_llama3_8b_mixed_every_row():
 
 def test_decode_heavy_every_decode():
     # the split-KV kernel in a launch of its own (K staged through LDS), every
-    # one of the 256 decodes and its chunks' merge
+    # one of the 256 decodes, most of them split into chunks and merged
     spec = synth.full_config(3)
     _, plan = run_dense(3, list(range(spec.bs)), every_row)
     info = plan.info()
-    assert info["num_prefill_items"] == 0 and info["num_merge_tokens"] > 200
+    assert info["num_prefill_items"] == 0 and info["num_merge_tokens"] > spec.bs // 2
 
 
 def test_chunked_prefill_one_chunk_and_every_decode():
